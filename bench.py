@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the DiT long-sequence attention hot path on one MI355X.
+
+Headline (the JSON line's value): attention forward with LSE on the FLUX.1 1024^2
+sequence, B=1, N=4608 (4096 image + 512 text tokens), 24 heads of 128, bf16 inputs
+with logits of standard deviation about 3, non-causal; one step = one attn_fwd_lse
+call over the whole sequence; value = 4*N*N*H*D flops / step time, in TFLOP/s.
+
+Legs timed in the same run and reported under "legs":
+  wan5b       attention at N=27280 (Wan2.2-TI2V-5B video tokens), 24 x 128
+  flux_ring4  one GPU's FLUX Ring-4 share: Ulysses-4 permute of the Q shards, then
+              Q[1152] x 4 KV chunks of 1152 through attn_fwd_lse (f32 partials), then the
+              LSE merge; each kernel's time and rate
+  wan14b_u8   one GPU's Wan2.1-14B Ulysses-8 share: N=75600, 5 heads, 8 KV chunks of 9450
+              + merge
+  permute_wan14b  the Ulysses-8 permute at Wan2.1-14B 720p, [8,1,9450,40,128] -> [8,1,75600,5,128]
+
+Inputs are seeded synthetic tensors (no dataset, no weights) already resident in
+HBM when a timed region starts.  Times come from HIP events recorded on the stream
+the kernels are launched on.  "roofline" describes the headline kernel;
+"cpu_baseline" times the fp64 CPU oracle on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_flux_N4608_H24_D128_pmc.txt")
+ATTN_SRC = os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc", "attn_fwd.hip")
+
+
+def err(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="wan5b,flux_ring4,wan14b_u8,permute_wan14b",
+                    help="comma list of extra legs (or 'none'); 'copy' adds a plain copy kernel "
+                         "used to calibrate HBM counters")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP-event timing of work enqueued on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def time(self, fn, reps, warmup=0):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for _ in range(reps):
+            fn()
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps  # ms per call
+
+
+def pmc_traffic():
+    """HBM bytes per launch of the headline kernel from the committed rocprofv3 counter
+    summary, or None when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    m = re.search(r"^source_sha256:\s*(\w+)", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not t or m.group(1) != sha:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, target_s):
+    import numpy as np
+    import oracle
+    import synthetic
+    q, k, v = synthetic.workload_qkv(w)
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    per_row = 4.0 * w.Nkv * w.D
+    n = 256
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, synthetic.sample_rows(11, w.B, w.H, w.Nq, n))
+    dt = time.perf_counter() - t0
+    n2 = int(min(w.B * w.H * w.Nq, max(n, n * target_s / max(dt, 1e-3))))
+    rows = synthetic.sample_rows(12, w.B, w.H, w.Nq, n2)
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, rows)
+    dt = time.perf_counter() - t0
+    return {"value": per_row * len(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d query rows (seeded, of %d) of the %s workload, each against all %d keys, "
+                      "fp64; %.1f s" % (len(rows), w.B * w.H * w.Nq, w.name, w.Nkv, dt),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE=%d)." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import diffusion_transformer_long_amd as dtl
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    legs_req = [] if args.legs == "none" else [x for x in args.legs.split(",") if x]
+
+    # ---------------------------------------------------------------- headline
+    w = synthetic.FLUX
+    err("[bench] headline %s: generating inputs" % w.name)
+    q, k, v = (t.to(dev) for t in synthetic.workload_qkv(w))
+    o = torch.empty((w.B, w.Nq, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+
+    def step():
+        dtl.attn_fwd_lse(q, k, v, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    err("[bench] headline: %.3f ms/step (wall), %.3f ms/launch (events), %.1f TFLOP/s"
+        % (ms_per_step, kernel_ms, achieved))
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": pmc_traffic(),
+                "kernel": "attn_fwd_kernel<128,bf16> on %s" % w.name,
+                "flops_per_launch": w.flops,
+                "algorithmic_bytes_per_launch": 2 * (3 + 1) * w.B * w.Nq * w.H * w.D + 4 * w.B * w.H * w.Nq}
+    del q, k, v, o, lse
+
+    legs = {}
+
+    # ---------------------------------------------------------------- wan5b
+    if "wan5b" in legs_req:
+        w5 = synthetic.WAN5B
+        err("[bench] leg wan5b: generating inputs")
+        q, k, v = (t.to(dev) for t in synthetic.workload_qkv(w5))
+        o = torch.empty((w5.B, w5.Nq, w5.H, w5.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w5.B, w5.H, w5.Nq), dtype=torch.float32, device=dev)
+        ms = timer.time(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), reps=max(3, args.steps // 4),
+                        warmup=2)
+        tf = w5.flops / (ms * 1e-3) / 1e12
+        legs["wan5b"] = {"workload": w5.name, "attn_ms": round(ms, 4), "attn_tflops": round(tf, 2),
+                         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        err("[bench] wan5b: %.3f ms, %.1f TFLOP/s" % (ms, tf))
+        del q, k, v, o, lse
+
+    # ---------------------------------------------------------------- flux ring-4 share
+    if "flux_ring4" in legs_req:
+        w3 = synthetic.FLUX_RING4
+        err("[bench] leg flux_ring4")
+        qf, k, v = (t.to(dev) for t in synthetic.workload_qkv(synthetic.FLUX))
+        shards = qf.reshape(1, 4, w3.Nq, w3.H, w3.D).transpose(0, 1).contiguous()
+        q = qf[:, :w3.Nq].contiguous()
+        C = w3.chunk_len
+        # rotate buffer sets so each rep of the bandwidth kernels misses the 256 MB MALL
+        nrot = 10
+        perm_out = [torch.empty((4, 1, w3.Nkv, w3.H // 4, w3.D), dtype=torch.bfloat16, device=dev) for _ in range(nrot)]
+        perm_in = [shards.clone() for _ in range(nrot)]
+        parts = [torch.empty((w3.chunks, 1, w3.Nq, w3.H, w3.D), dtype=torch.float32, device=dev) for _ in range(nrot)]
+        lparts = [torch.empty((w3.chunks, 1, w3.H, w3.Nq), dtype=torch.float32, device=dev) for _ in range(nrot)]
+        o = torch.empty((1, w3.Nq, w3.H, w3.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, w3.H, w3.Nq), dtype=torch.float32, device=dev)
+        for i in range(nrot):
+            dtl.attn_fwd_lse_kv_chunks(q, k, v, w3.chunks, parts[i], lparts[i])
+        ctr = [0]
+
+        def rot():
+            ctr[0] = (ctr[0] + 1) % nrot
+            return ctr[0]
+
+        reps = 3 * nrot
+        ms_perm = timer.time(lambda: dtl.seq_to_head_permute(perm_in[rot()], 4, out=perm_out[ctr[0]]), reps, warmup=nrot)
+        ms_chunk = timer.time(lambda: dtl.attn_fwd_lse(q, k[:, :C], v[:, :C], o=parts[0][0], lse=lparts[0][0]),
+                              reps=20, warmup=3)
+        ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts[rot()], lparts[ctr[0]], o=o, lse=lse), reps, warmup=nrot)
+
+        def share_step():
+            dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
+            dtl.attn_fwd_lse_kv_chunks(q, k, v, w3.chunks, parts[0], lparts[0])
+            dtl.attn_merge_lse(parts[0], lparts[0], o=o, lse=lse)
+        ms_step = timer.time(share_step, reps=10, warmup=2)
+        perm_bytes = 2 * shards.numel() * 2
+        merge_bytes = (w3.chunks * w3.Nq * w3.H * (w3.D + 1) * 4) + w3.Nq * w3.H * (w3.D * 2 + 4)
+        chunk_flops = 4.0 * w3.Nq * C * w3.H * w3.D
+        legs["flux_ring4"] = {
+            "workload": w3.name, "step_ms": round(ms_step, 4),
+            "step_tflops": round(w3.flops / (ms_step * 1e-3) / 1e12, 2),
+            "permute_ms": round(ms_perm, 4), "permute_gbs": round(perm_bytes / (ms_perm * 1e-3) / 1e9, 1),
+            "permute_bytes": perm_bytes,
+            "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
+            "merge_ms": round(ms_merge, 4), "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
+            "merge_bytes": merge_bytes, "rotation_buffers": nrot}
+        err("[bench] flux_ring4: %s" % legs["flux_ring4"])
+        del qf, k, v, shards, q, perm_out, perm_in, parts, lparts, o, lse
+
+    # ---------------------------------------------------------------- wan14b u8 share
+    if "wan14b_u8" in legs_req:
+        w5 = synthetic.WAN14B_U8
+        err("[bench] leg wan14b_u8: generating inputs")
+        q, k, v = (t.to(dev) for t in synthetic.workload_qkv(w5))
+        C = w5.chunk_len
+        parts = torch.empty((w5.chunks, 1, w5.Nq, w5.H, w5.D), dtype=torch.float32, device=dev)
+        lparts = torch.empty((w5.chunks, 1, w5.H, w5.Nq), dtype=torch.float32, device=dev)
+        o = torch.empty((1, w5.Nq, w5.H, w5.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, w5.H, w5.Nq), dtype=torch.float32, device=dev)
+        dtl.attn_fwd_lse_kv_chunks(q, k, v, w5.chunks, parts, lparts)
+        ms_chunk = timer.time(lambda: dtl.attn_fwd_lse(q, k[:, :C], v[:, :C], o=parts[0], lse=lparts[0]),
+                              reps=4, warmup=1)
+        ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts, lparts, o=o, lse=lse), reps=10, warmup=2)
+        ms_step = timer.time(lambda: dtl.ring_attention(q, k, v, w5.chunks, o_parts=parts, lse_parts=lparts,
+                                                         o=o, lse=lse), reps=2, warmup=1)
+        merge_bytes = (w5.chunks * w5.Nq * w5.H * (w5.D + 1) * 4) + w5.Nq * w5.H * (w5.D * 2 + 4)
+        chunk_flops = 4.0 * w5.Nq * C * w5.H * w5.D
+        legs["wan14b_u8"] = {
+            "workload": w5.name, "step_ms": round(ms_step, 3),
+            "step_tflops": round(w5.flops / (ms_step * 1e-3) / 1e12, 2),
+            "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
+            "merge_ms": round(ms_merge, 4), "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
+            "merge_bytes": merge_bytes, "merge_frac_of_hbm": round(merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        err("[bench] wan14b_u8: %s" % legs["wan14b_u8"])
+        del q, k, v, parts, lparts, o, lse
+
+    # ---------------------------------------------------------------- permute at Wan-14B U8
+    if "permute_wan14b" in legs_req:
+        p, Ns, H, D = 8, 9450, 40, 128
+        err("[bench] leg permute_wan14b")
+        x = torch.empty((p, 1, Ns, H, D), dtype=torch.bfloat16, device=dev).normal_()
+        out = torch.empty((p, 1, Ns * p, H // p, D), dtype=torch.bfloat16, device=dev)
+        ms = timer.time(lambda: dtl.seq_to_head_permute(x, p, out=out), reps=10, warmup=2)
+        nbytes = 2 * x.numel() * 2
+        legs["permute_wan14b"] = {"shape": "[8,1,9450,40,128]->[8,1,75600,5,128] bf16", "ms": round(ms, 4),
+                                  "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
+                                  "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        err("[bench] permute_wan14b: %s" % legs["permute_wan14b"])
+        del x, out
+
+    # ---------------------------------------------------------------- copy (counter calibration)
+    if "copy" in legs_req:
+        nb = 1 << 30
+        a = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        ms = timer.time(lambda: b.copy_(a), reps=5, warmup=2)
+        legs["copy"] = {"bytes_read": nb, "bytes_written": nb, "ms": round(ms, 4),
+                        "gbs": round(2 * nb / (ms * 1e-3) / 1e9, 1)}
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        err("[bench] cpu baseline (oracle on host cores)")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        err("[bench] cpu baseline: %s" % cpu)
+
+    line = {
+        "metric": "attention TFLOP/s + % bf16 MFMA peak at N=4608 and N=27280, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "seq_len": w.Nq, "heads": w.H, "head_dim": w.D,
+                   "k_scale": w.k_scale, "causal": False, "o_dtype": "bf16", "lse_dtype": "f32",
+                   "parallelism": "none (one GPU's full sequence)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

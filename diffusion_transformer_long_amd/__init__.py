@@ -1,0 +1,206 @@
+"""Python binding of libdtl.so: DiT long-sequence attention on one MI355X (gfx950).
+
+Argument marshalling only.  Every function here checks tensor devices, dtypes and
+shapes, allocates outputs with torch when none are given, and calls the C ABI of
+``include/dtl.h`` with raw device pointers and torch's current HIP stream.  All
+arithmetic runs in the HIP kernels.  Importing this package fails when the
+library has not been built; there is no fallback.
+
+Entry points (same names as the C ABI):
+  attn_fwd_lse(q, k, v, ...)            -> (o, lse)
+  attn_merge_lse(o_parts, lse_parts, ...) -> (o, lse)
+  seq_to_head_permute(x, p, ...)        -> out
+and two drivers that only sequence those calls:
+  attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  one call per KV chunk
+  ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdtl.so")
+
+DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
+DTL_BF16, DTL_F32 = 0, 1
+
+EXPORTS = ("attn_fwd_lse", "attn_merge_lse", "seq_to_head_permute", "dtl_status_string")
+
+
+class DtlError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libdtl.so is not built (%s). Build it with `python __graft_entry__.py` or "
+            "`python -m diffusion_transformer_long_amd.build`." % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_lse.restype = i
+    lib.attn_merge_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.attn_merge_lse.restype = i
+    lib.seq_to_head_permute.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+    lib.seq_to_head_permute.restype = i
+    lib.dtl_status_string.argtypes = [i]
+    lib.dtl_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load_library()
+
+
+def status_string(status: int) -> str:
+    return lib.dtl_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != DTL_OK:
+        raise DtlError(status, status_string(status))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return DTL_BF16
+    if dt == torch.float32:
+        return DTL_F32
+    raise TypeError("unsupported dtype %s (bf16 or f32)" % dt)
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+
+
+def attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 softmax_scale: Optional[float] = None, o_dtype: torch.dtype = torch.bfloat16,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o = softmax(q k^T * scale) v and lse = ln sum exp(scale q.k) per (b, h, row).
+    q [B,Nq,H,D], k/v [B,Nkv,H,D] bf16 -> o [B,Nq,H,D] (o_dtype), lse [B,H,Nq] f32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.bfloat16, 4)
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, D) or tuple(v.shape) != (B, Nkv, H, D):
+        raise ValueError("k and v must be [B, Nkv, H, D] matching q %s" % (tuple(q.shape),))
+    if o is None:
+        o = torch.empty((B, Nq, H, D), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _dev(o, "o", None, 4)
+    _dev(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Nq, H, D) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must be [B,Nq,H,D] and lse [B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Nq, Nkv, H, D, scale, _dtype_code(o.dtype), _stream(q, stream)))
+    return o, lse
+
+
+def attn_merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor,
+                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.bfloat16, write_lse: bool = True,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact merge of partials over disjoint key sets: o_parts [P,B,N,H,D] (f32 or bf16),
+    lse_parts [P,B,H,N] f32 -> o [B,N,H,D] (out_dtype), lse [B,H,N] f32 (or None)."""
+    _dev(o_parts, "o_parts", None, 5)
+    _dev(lse_parts, "lse_parts", torch.float32, 4)
+    P, B, N, H, D = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, H, N):
+        raise ValueError("lse_parts must be [P,B,H,N] = %s" % ((P, B, H, N),))
+    if o is None:
+        o = torch.empty((B, N, H, D), dtype=out_dtype, device=o_parts.device)
+    _dev(o, "o", None, 4)
+    if tuple(o.shape) != (B, N, H, D):
+        raise ValueError("o must be [B,N,H,D]")
+    if write_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B,H,N]")
+    _check(lib.attn_merge_lse(o_parts.data_ptr(), lse_parts.data_ptr(), o.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              P, B, N, H, D, _dtype_code(o_parts.dtype), _dtype_code(o.dtype),
+                              _stream(o_parts, stream)))
+    return o, lse
+
+
+def seq_to_head_permute(x: torch.Tensor, p: int, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Ulysses seq->head permute: x [p,B,N/p,H,D] (p sequence shards) ->
+    out [p,B,N,H/p,D] (p head shards).  Any 1/2/4/8-byte dtype; bit-exact."""
+    _dev(x, "x", None, 5)
+    p_, B, Ns, H, D = x.shape
+    if p_ != p:
+        raise ValueError("x.shape[0] must equal p")
+    if H % p != 0:
+        raise ValueError("p must divide the head count")
+    N = Ns * p
+    if out is None:
+        out = torch.empty((p, B, N, H // p, D), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype, 5)
+    if tuple(out.shape) != (p, B, N, H // p, D):
+        raise ValueError("out must be [p,B,N,H/p,D]")
+    _check(lib.seq_to_head_permute(x.data_ptr(), out.data_ptr(), p, B, N, H, D,
+                                   x.element_size(), _stream(x, stream)))
+    return out
+
+
+def attn_fwd_lse_kv_chunks(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: int,
+                           o_parts: Optional[torch.Tensor] = None,
+                           lse_parts: Optional[torch.Tensor] = None,
+                           softmax_scale: Optional[float] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One attn_fwd_lse call per contiguous KV chunk [t*C, (t+1)*C), as the rounds of Ring
+    attention see them; f32 partials o_parts [P,B,Nq,H,D], lse_parts [P,B,H,Nq].  B must
+    be 1 so that a chunk is a contiguous view of k and v."""
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    if B != 1:
+        raise ValueError("KV chunking by views needs B == 1")
+    if Nkv % chunks != 0:
+        raise ValueError("chunks must divide Nkv")
+    C = Nkv // chunks
+    if o_parts is None:
+        o_parts = torch.empty((chunks, B, Nq, H, D), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((chunks, B, H, Nq), dtype=torch.float32, device=q.device)
+    for t in range(chunks):
+        attn_fwd_lse(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C], o=o_parts[t],
+                     lse=lse_parts[t], softmax_scale=softmax_scale, stream=stream)
+    return o_parts, lse_parts
+
+
+def ring_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: int,
+                   out_dtype: torch.dtype = torch.bfloat16, softmax_scale: Optional[float] = None,
+                   o_parts: Optional[torch.Tensor] = None, lse_parts: Optional[torch.Tensor] = None,
+                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention over all keys computed as Ring attention's rounds on one GPU: per-chunk
+    partials, then the LSE merge."""
+    o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
+                                                softmax_scale, stream)
+    return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype, stream=stream)

@@ -1,0 +1,301 @@
+// Attention forward with per-row log-sum-exp for gfx950 (MI355X).
+//
+// Computes o = softmax(q k^T * scale) v and lse = ln sum_j exp(scale q.k_j) per
+// (batch, head, query row), non-causal, on BSND bf16 tensors (MindIE SD "多卡并行"
+// page, Ring Sequence Parallel usage example, for the formula; "AIGC 分布式推理：从
+// Wan2.2 理解 DP/TP/CP/SP/PP", CP section, for head independence and every query
+// seeing every key).  The key loop is the online-softmax accumulation that Ring
+// attention also performs across rounds (arganzheng.life, multi-GPU diffusion
+// parallelism, section 4.2).
+//
+// Work decomposition
+//   workgroup = 4 waves = 128 query rows of one (batch, head); wave w owns rows
+//   [32w, 32w+32).  Keys are consumed 64 per iteration from a double-buffered LDS tile.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] B[16x32]):
+//   S^T = K Q^T:  A = a 32-key block of K (lane l: key row l%32, 8 head_dim values
+//                 at 8*(l/32)), B = Q^T (lane l: query l%32, the same 8 head_dim).
+//                 The result puts one query per lane: lane l holds 16 keys of query
+//                 l%32, the other 16 keys of that query sit in lane l^32.  Row max and
+//                 row sum are in-lane plus one exchange between the lane halves.
+//   O^T += V^T P^T: B = P^T comes straight from the S^T registers (rounded to bf16),
+//                 because the B operand layout (lane l: column l%32, 8 consecutive k)
+//                 matches them once K rows are stored in LDS in a permuted order (rows
+//                 m and sigma(m) swap bits 2 and 3), so that register i of lane l holds
+//                 key 16*(i/8) + 8*(l/32) + i%8 of its 32-key block.  A = V^T needs 8
+//                 consecutive keys of one head_dim column per lane, so V is transposed
+//                 on its way into LDS (4 keys x 8 columns per thread, in registers).
+//   The O^T accumulator also keeps one query per lane, so the softmax rescale is a
+//   per-lane scalar.
+//
+// Softmax in base 2: p = exp2(s * scale*log2(e) - m), m the running max of the scaled
+// logits in log2 units.  The running max is only moved when some row's tile max
+// exceeds it by more than 8 (the accumulators are then rescaled); otherwise p <= 2^8,
+// which f32 and bf16 hold without overflow.  The result is the same softmax, since
+// numerator and denominator share the reference m.
+#include "common.h"
+
+namespace dtl {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlockM = kWaves * 32;   // query rows per workgroup
+constexpr int kBlockN = 64;            // keys per iteration
+constexpr float kRescaleThreshold = 8.0f;
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct Tile {
+    static constexpr int kRow = D + 8;           // K row stride in LDS (bf16 units, +16 B pad)
+    static constexpr int vRow = kBlockN + 8;     // V^T row stride in LDS (bf16 units, +16 B pad)
+    static constexpr int kChunks = kBlockN * D / 8 / kThreads;  // 16-B K chunks per thread
+    static constexpr int vBlocks = (kBlockN / 4) * (D / 8);     // 4-key x 8-column V blocks
+    static constexpr int vPerThread = (vBlocks + kThreads - 1) / kThreads;
+    static_assert(kBlockN * D / 8 % kThreads == 0, "K tile must split evenly");
+};
+
+// LDS row of key `key` of a tile: bits 2 and 3 swapped (an involution).
+__device__ __forceinline__ int krow_slot(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 2)
+void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, void* __restrict__ o,
+                     float* __restrict__ lse, int Nq, int Nkv, int H, float scale_log2,
+                     int n_qtiles, int total) {
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::kRow];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::vRow];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 5;   // lane half
+    const int r = lane & 31;
+
+    const int logical = xcd_contiguous(blockIdx.x, total);
+    const int qt = logical % n_qtiles;
+    const int bh = logical / n_qtiles;
+    const int h = bh % H;
+    const int b = bh / H;
+
+    const long tok_stride = (long)H * D;
+    const uint16_t* kbase = k + ((long)b * Nkv * H + h) * D;
+    const uint16_t* vbase = v + ((long)b * Nkv * H + h) * D;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    // Q^T fragments, held for the whole key loop.
+    const int qrow = qt * kBlockM + wave * 32 + r;
+    bf16x8 qf[D / 16];
+    {
+        const uint16_t* qp = q + (((long)b * Nq + qrow) * H + h) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : zero4;
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    u32x4 kreg[T::kChunks];
+    u32x4 vreg[T::vPerThread][4];
+
+    auto load_tile = [&](int kv0) {
+#pragma unroll
+        for (int c = 0; c < T::kChunks; ++c) {
+            const int idx = tid + c * kThreads;
+            const int row = idx / (D / 8), col = idx % (D / 8);
+            const int key = kv0 + row;
+            kreg[c] = key < Nkv
+                ? *reinterpret_cast<const u32x4*>(kbase + (long)key * tok_stride + col * 8)
+                : zero4;
+        }
+#pragma unroll
+        for (int c = 0; c < T::vPerThread; ++c) {
+            const int blk = tid + c * kThreads;
+            if (blk < T::vBlocks) {
+                const int kg = blk % (kBlockN / 4), dg = blk / (kBlockN / 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = kv0 + kg * 4 + j;
+                    vreg[c][j] = key < Nkv
+                        ? *reinterpret_cast<const u32x4*>(vbase + (long)key * tok_stride + dg * 8)
+                        : zero4;
+                }
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < T::kChunks; ++c) {
+            const int idx = tid + c * kThreads;
+            const int row = idx / (D / 8), col = idx % (D / 8);
+            *reinterpret_cast<u32x4*>(&sK[buf][krow_slot(row) * T::kRow + col * 8]) = kreg[c];
+        }
+#pragma unroll
+        for (int c = 0; c < T::vPerThread; ++c) {
+            const int blk = tid + c * kThreads;
+            if (blk < T::vBlocks) {
+                const int kg = blk % (kBlockN / 4), dg = blk / (kBlockN / 4);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t a0 = vreg[c][0][w], a1 = vreg[c][1][w];
+                    const uint32_t a2 = vreg[c][2][w], a3 = vreg[c][3][w];
+                    // column 2w of the 8: the low halves of the 4 keys; column 2w+1: the high halves
+                    u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+                    u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+                    *reinterpret_cast<u32x2*>(&sV[buf][(dg * 8 + 2 * w) * T::vRow + kg * 4]) = lo;
+                    *reinterpret_cast<u32x2*>(&sV[buf][(dg * 8 + 2 * w + 1) * T::vRow + kg * 4]) = hi;
+                }
+            }
+        }
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    float m_run = -INFINITY;  // reference max of this lane's query row (log2 units)
+    float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
+
+    const int n_tiles = (Nkv + kBlockN - 1) / kBlockN;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int it = 0; it < n_tiles; ++it) {
+        const int buf = it & 1;
+        const int kv0 = it * kBlockN;
+        const bool has_next = it + 1 < n_tiles;
+        if (has_next) load_tile(kv0 + kBlockN);
+
+        const uint16_t* sk = sK[buf];
+        const uint16_t* sv = sV[buf];
+
+        // S^T for two 32-key blocks.
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + r) * T::kRow + ks * 16 + g * 8);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+            }
+        }
+
+        if (kv0 + kBlockN > Nkv) {  // ragged last tile: keys past the end get weight 0
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kv0 + kb * 32 + 16 * (i / 8) + 8 * g + (i % 8);
+                    if (key >= Nkv) s[kb][i] = -INFINITY;
+                }
+        }
+
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx2 = mx * scale_log2;
+        if (__any(mx2 > m_run + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_run, mx2);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+            m_run = m_new;
+        }
+
+        bf16x8 pf[2][2];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x8 e;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][hf * 8 + i], scale_log2, -m_run));
+                    lsum += e[i];
+                }
+                pf[kb][hf] = __builtin_convertvector(e, bf16x8);
+            }
+        l_run += lsum;
+
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        sv + (db * 32 + r) * T::vRow + kb * 32 + hf * 16 + g * 8);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hf], acc[db], 0, 0, 0);
+                }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qrow < Nq) {
+        const float inv = 1.0f / l_tot;
+        const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                f32x4 x = {acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
+                           acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv};
+                const long off = obase + db * 32 + 8 * i4;
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
+                } else {
+                    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) =
+                        __builtin_convertvector(x, bf16x4);
+                }
+            }
+        if (g == 0)
+            lse[((long)b * H + h) * Nq + qrow] = (m_run + log2f(l_tot)) * 0.693147180559945309f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Nq, int Nkv, int H, int D, float scale, bool out_f32,
+                           hipStream_t stream) {
+    const int n_qtiles = (Nq + kBlockM - 1) / kBlockM;
+    const int total = n_qtiles * H * B;  // the caller has checked that this fits an int
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    const dim3 grid(total), block(kThreads);
+    auto qq = static_cast<const uint16_t*>(q);
+    auto kk = static_cast<const uint16_t*>(k);
+    auto vv = static_cast<const uint16_t*>(v);
+    if (D == 128) {
+        if (out_f32)
+            attn_fwd_kernel<128, true><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
+        else
+            attn_fwd_kernel<128, false><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
+    } else {
+        if (out_f32)
+            attn_fwd_kernel<64, true><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
+        else
+            attn_fwd_kernel<64, false><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dtl

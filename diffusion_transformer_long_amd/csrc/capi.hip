@@ -1,0 +1,104 @@
+// C ABI of libdtl.so: host-side validation, then one kernel launch per call.
+// Declarations and the contract of each entry point are in include/dtl.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "dtl.h"
+#include "common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges)
+bool overlap(const void* a, long na, const void* b, long nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+constexpr long kIntMax = 2147483647l;
+
+}  // namespace
+
+extern "C" {
+
+const char* dtl_status_string(dtl_status s) {
+    switch (s) {
+        case DTL_OK: return "DTL_OK";
+        case DTL_ERR_INVALID_ARG: return "DTL_ERR_INVALID_ARG: invalid argument";
+        case DTL_ERR_UNSUPPORTED: return "DTL_ERR_UNSUPPORTED: not supported by this build";
+        case DTL_ERR_HIP: return "DTL_ERR_HIP: HIP runtime error at launch";
+    }
+    return "DTL_ERR_UNKNOWN: unknown status";
+}
+
+dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Nq, int Nkv, int H, int D, float softmax_scale,
+                        dtl_dtype o_dtype, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return DTL_ERR_INVALID_ARG;
+    if (B <= 0 || Nq <= 0 || Nkv <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DTL_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return DTL_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return DTL_ERR_UNSUPPORTED;
+    if (o_dtype != DTL_BF16 && o_dtype != DTL_F32) return DTL_ERR_UNSUPPORTED;
+    const long q_bytes = (long)B * Nq * H * D * 2;
+    const long kv_bytes = (long)B * Nkv * H * D * 2;
+    const long o_bytes = (long)B * Nq * H * D * (o_dtype == DTL_F32 ? 4 : 2);
+    const long l_bytes = (long)B * H * Nq * 4;
+    if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
+        overlap(o, o_bytes, v, kv_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
+        overlap(lse, l_bytes, q, q_bytes) || overlap(lse, l_bytes, k, kv_bytes) ||
+        overlap(lse, l_bytes, v, kv_bytes))
+        return DTL_ERR_INVALID_ARG;
+    const long tiles = ((long)Nq + 127) / 128 * H * B;
+    if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)B * Nq * H > kIntMax)
+        return DTL_ERR_INVALID_ARG;
+    hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, B, Nq, Nkv, H, D, softmax_scale,
+                                        o_dtype == DTL_F32, stream);
+    return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
+dtl_status attn_merge_lse(const void* o_parts, const float* lse_parts, void* o, float* lse,
+                          int P, int B, int N, int H, int D, dtl_dtype parts_dtype,
+                          dtl_dtype out_dtype, hipStream_t stream) {
+    if (!o_parts || !lse_parts || !o) return DTL_ERR_INVALID_ARG;
+    if (P <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || (lse && !aligned16(lse)))
+        return DTL_ERR_INVALID_ARG;
+    if (D % 8 != 0) return DTL_ERR_UNSUPPORTED;
+    if ((parts_dtype != DTL_BF16 && parts_dtype != DTL_F32) ||
+        (out_dtype != DTL_BF16 && out_dtype != DTL_F32))
+        return DTL_ERR_UNSUPPORTED;
+    const long rows = (long)B * N * H;
+    const long parts_bytes = (long)P * rows * D * (parts_dtype == DTL_F32 ? 4 : 2);
+    const long lp_bytes = (long)P * rows * 4;
+    const long o_bytes = rows * D * (out_dtype == DTL_F32 ? 4 : 2);
+    const long l_bytes = rows * 4;
+    if (overlap(o, o_bytes, o_parts, parts_bytes) || overlap(o, o_bytes, lse_parts, lp_bytes))
+        return DTL_ERR_INVALID_ARG;
+    if (lse && (overlap(lse, l_bytes, o_parts, parts_bytes) || overlap(lse, l_bytes, lse_parts, lp_bytes) ||
+                overlap(lse, l_bytes, o, o_bytes)))
+        return DTL_ERR_INVALID_ARG;
+    if (rows * (D / 8) > kIntMax || (long)B * H * N > kIntMax) return DTL_ERR_INVALID_ARG;
+    hipError_t e = dtl::launch_merge(o_parts, lse_parts, o, lse, P, B, N, H, D,
+                                     parts_dtype == DTL_F32, out_dtype == DTL_F32, stream);
+    return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
+dtl_status seq_to_head_permute(const void* in, void* out, int p, int B, int N, int H, int D,
+                               int elem_bytes, hipStream_t stream) {
+    if (!in || !out) return DTL_ERR_INVALID_ARG;
+    if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
+    if (N % p != 0 || H % p != 0) return DTL_ERR_INVALID_ARG;
+    if (!aligned16(in) || !aligned16(out)) return DTL_ERR_INVALID_ARG;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+        return DTL_ERR_UNSUPPORTED;
+    const long bytes = (long)B * N * H * D * elem_bytes;
+    if (overlap(in, bytes, out, bytes)) return DTL_ERR_INVALID_ARG;
+    if ((long)B * N * H * D / 256 + 1 > kIntMax) return DTL_ERR_INVALID_ARG;
+    hipError_t e = dtl::launch_permute(in, out, p, B, N, H, D, elem_bytes, stream);
+    return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
+}  // extern "C"

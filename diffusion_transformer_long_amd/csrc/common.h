@@ -1,0 +1,42 @@
+// Internal declarations shared by the HIP sources of libdtl.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dtl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// gfx950 dispatches consecutive workgroup ids round-robin over its 8 XCDs, each with
+// its own L2.  Remapping the id so that each XCD receives one contiguous range of
+// logical tiles keeps the tiles that share K/V (same head) on the same L2.
+constexpr int kNumXcd = 8;
+
+__host__ __device__ __forceinline__ int xcd_contiguous(int pid, int total) {
+    const int per = (total + kNumXcd - 1) / kNumXcd;
+    const int rem = total % kNumXcd;
+    const int full = rem == 0 ? kNumXcd : rem;  // XCDs that receive `per` ids
+    const int xcd = pid % kNumXcd;
+    const int local = pid / kNumXcd;
+    if (xcd < full) return xcd * per + local;
+    return full * per + (xcd - full) * (per - 1) + local;
+}
+
+// Launchers (validated arguments only; each returns hipGetLastError()).
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Nq, int Nkv, int H, int D, float scale, bool out_f32,
+                           hipStream_t stream);
+hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
+                        int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,
+                        hipStream_t stream);
+hipError_t launch_permute(const void* in, void* out, int p, int B, int N, int H, int D,
+                          int elem_bytes, hipStream_t stream);
+
+}  // namespace dtl

@@ -1,0 +1,132 @@
+/*
+ * dtl.h - C ABI of libdtl.so: the per-GPU hot path of sequence-parallel DiT
+ * self-attention on one AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller (for example
+ *     the storage of a torch tensor).  The library never allocates, frees, or keeps
+ *     a pointer after the call returns.
+ *   - Tensors are dense and row-major in the shapes given; there are no strides.
+ *     Every pointer must be 16-byte aligned.
+ *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.
+ *   - Calls are asynchronous on `stream` (NULL selects the null stream).  They do
+ *     not synchronize and hold no global state, so calls on different streams may
+ *     run concurrently as long as their buffers do not overlap.
+ *   - Arguments are validated on the host before anything is launched.  On a
+ *     validation error nothing is launched and nothing is written.  DTL_ERR_HIP is
+ *     returned when the kernel launch itself reports an error.  Device faults surface,
+ *     as for any HIP stream work, at the caller's next synchronization.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef DTL_H
+#define DTL_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DTL_OK = 0,
+    DTL_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misalignment, overlap, bad divisibility */
+    DTL_ERR_UNSUPPORTED = 2,  /* valid request outside what this build implements (head_dim, dtype) */
+    DTL_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+} dtl_status;
+
+typedef enum {
+    DTL_BF16 = 0,
+    DTL_F32 = 1
+} dtl_dtype;
+
+/*
+ * attn_fwd_lse - attention forward with per-row log-sum-exp.
+ *
+ * Computes, independently for every batch b, head h and query row i, over all
+ * keys j in [0, Nkv) (non-causal: every query sees every key):
+ *     s_ij        = softmax_scale * sum_d q[b,i,h,d] * k[b,j,h,d]
+ *     o[b,i,h,:]  = sum_j exp(s_ij) * v[b,j,h,:] / sum_j exp(s_ij)
+ *     lse[b,h,i]  = ln sum_j exp(s_ij)                 (natural log, scaled logits)
+ * This is softmax(q k^T / sqrt(d)) v per head as the MindIE SD "多卡并行" page
+ * states it (Ring Sequence Parallel section, usage example), with heads
+ * independent and every query attending to every key ("AIGC 分布式推理：从 Wan2.2
+ * 理解 DP/TP/CP/SP/PP", CP section).  The LSE is what lets partial results over
+ * separate key chunks be combined exactly (attn_merge_lse).
+ *
+ *   q    bf16 [B, Nq,  H, D]   (BSND: token-major, heads then head_dim)
+ *   k    bf16 [B, Nkv, H, D]
+ *   v    bf16 [B, Nkv, H, D]
+ *   o    o_dtype [B, Nq, H, D]  bf16 (rounded to nearest even) for a final result,
+ *                               f32 for a partial that will be merged
+ *   lse  f32 [B, H, Nq]
+ *   softmax_scale  finite and > 0; callers pass 1/sqrt(D)
+ *
+ * Arithmetic: bf16 products with f32 accumulation for q.k and p.v; the softmax
+ * weights are kept in f32 for the row sum and rounded to bf16 for the p.v product.
+ * Errors: DTL_ERR_INVALID_ARG for null pointers, any size <= 0, a scale that is not
+ * finite and positive, misaligned pointers, or an output overlapping an input or the
+ * other output; DTL_ERR_UNSUPPORTED for D not in {64, 128} or another o_dtype.
+ */
+dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
+                        void *o, float *lse,
+                        int B, int Nq, int Nkv, int H, int D,
+                        float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
+
+/*
+ * attn_merge_lse - exact merge of P partial attention results over disjoint key sets.
+ *
+ * For every (b, n, h), with parts t = 0..P-1:
+ *     L           = ln sum_t exp(lse_parts[t,b,h,n])
+ *     o[b,n,h,:]  = sum_t exp(lse_parts[t,b,h,n] - L) * o_parts[t,b,n,h,:]
+ *     lse[b,h,n]  = L
+ * This is the online-softmax accumulation that Ring attention performs across its
+ * rounds (arganzheng.life, multi-GPU diffusion parallelism, section 4.2 "Ring";
+ * MindIE SD "多卡并行" page, Ring Sequence Parallel section).  When the parts are
+ * attn_fwd_lse results over a partition of the keys, the merge equals attention
+ * over all keys.  A part with lse = -inf holds no keys and contributes nothing; a
+ * row whose parts are all -inf yields o = 0 and lse = -inf.
+ *
+ *   o_parts    parts_dtype [P, B, N, H, D]  (f32 recommended; bf16 accepted)
+ *   lse_parts  f32 [P, B, H, N]
+ *   o          out_dtype [B, N, H, D]
+ *   lse        f32 [B, H, N], or NULL to skip writing it
+ *
+ * Errors: DTL_ERR_INVALID_ARG for null inputs or o, sizes <= 0, misalignment, or an
+ * output overlapping an input; DTL_ERR_UNSUPPORTED for D not a multiple of 8 or a
+ * dtype outside {DTL_BF16, DTL_F32}.
+ */
+dtl_status attn_merge_lse(const void *o_parts, const float *lse_parts,
+                          void *o, float *lse,
+                          int P, int B, int N, int H, int D,
+                          dtl_dtype parts_dtype, dtl_dtype out_dtype, hipStream_t stream);
+
+/*
+ * seq_to_head_permute - the local data movement of a Ulysses all-to-all.
+ *
+ * Turns p sequence shards ("N/p tokens x all H heads" on each rank) into p head
+ * shards ("all N tokens x H/p heads"): head group j = heads [j*H/p, (j+1)*H/p),
+ * tokens concatenated in source-rank order (arganzheng.life section 4.1 and its
+ * figure; MindIE SD "多卡并行" page, Ulysses usage example: split the head axis
+ * into p parts, exchange, concatenate along tokens; "AIGC 分布式推理" CP section's
+ * [13640 tokens, 24 heads] -> [27280 tokens, 12 heads] at p = 2):
+ *     out[j][b][s*(N/p) + n][hh][d] = in[s][b][n][j*(H/p) + hh][d]
+ *
+ *   in   [p, B, N/p, H, D]    the p sequence shards, in rank order
+ *   out  [p, B, N, H/p, D]    the p head shards; out[j] is what rank j receives
+ *   elem_bytes  1, 2, 4 or 8 (2 for bf16); the copy is bit-exact
+ *
+ * Errors: DTL_ERR_INVALID_ARG for null or overlapping buffers, sizes <= 0,
+ * misalignment, p not dividing N or H; DTL_ERR_UNSUPPORTED for another elem_bytes.
+ */
+dtl_status seq_to_head_permute(const void *in, void *out,
+                               int p, int B, int N, int H, int D,
+                               int elem_bytes, hipStream_t stream);
+
+/* A static, human-readable name of a status code (never NULL). */
+const char *dtl_status_string(dtl_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTL_H */

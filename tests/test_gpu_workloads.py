@@ -1,0 +1,100 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the bench times.
+
+* tiny ring (N=256, 4 heads of 64, KV 4 x 64): full oracle; one full-sequence call and
+  the ring emulation (4 chunk calls + merge).
+* FLUX (N=4608, 24 x 128, K x 3): full-sequence call; a seeded sample of query rows
+  (first and last row of every head included) against the oracle row by row.
+* FLUX Ring-4 share: each of the 4 ranks' 1152-row Q blocks against the full K/V as
+  4 chunks of 1152 + merge, sampled rows; the Ulysses-4 permute of the four Q shards
+  [4,1,1152,24,128] -> [4,1,4608,6,128], bit-exact over the whole tensor.
+* Wan2.2-5B (N=27280, 24 x 128): full-sequence call, sampled rows.
+* Wan2.1-14B Ulysses-8 share (N=75600, 5 x 128, KV 8 x 9450): chunks + merge, sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import assert_close, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+SAMPLE_ROWS = 384
+
+
+def _check_rows(name, w, o, lse, q, k, v, n=SAMPLE_ROWS, seed=0):
+    rows = synthetic.sample_rows(seed or w.seed + 100, w.B, w.H, w.Nq, n)
+    o_ref, l_ref = oracle.attn_rows(q, k, v, rows)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    o_np = o.float().cpu().numpy()
+    l_np = lse.cpu().numpy()
+    assert_close(name + " O (%d rows)" % len(rows), o_np[b, i, h].astype(np.float64), o_ref)
+    assert_close(name + " LSE (%d rows)" % len(rows), l_np[b, h, i].astype(np.float64), l_ref)
+
+
+def test_tiny_ring_full_oracle():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.TINY_RING
+    log("workload %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)
+    o_ref, l_ref = oracle.attn(q, k, v)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert_close("full call O", to_np(o), o_ref)
+    assert_close("full call LSE", to_np(lse), l_ref)
+    o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
+    torch.cuda.synchronize()
+    assert_close("ring 4x64 O", to_np(o), o_ref)
+    assert_close("ring 4x64 LSE", to_np(lse), l_ref)
+
+
+def test_flux_full_sequence():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.FLUX
+    log("workload %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    _check_rows("flux", w, o, lse, q, k, v, n=1024)
+
+
+def test_flux_ring4_share_and_ulysses4_permute():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.FLUX_RING4
+    log("workload %s" % w.name)
+    qf, k, v = synthetic.workload_qkv(synthetic.FLUX)   # the share reuses FLUX's tensors
+    kd, vd = k.to(DEV), v.to(DEV)
+    for rank in range(4):
+        q = qf[:, rank * w.Nq:(rank + 1) * w.Nq].contiguous()
+        o, lse = dtl.ring_attention(q.to(DEV), kd, vd, w.chunks)
+        torch.cuda.synchronize()
+        _check_rows("ring4 rank%d" % rank, w, o, lse, q, k, v, n=256, seed=300 + rank)
+    shards = qf.reshape(1, 4, w.Nq, w.H, w.D).transpose(0, 1).contiguous()   # [4,1,1152,24,128]
+    out = dtl.seq_to_head_permute(shards.to(DEV), 4)
+    torch.cuda.synchronize()
+    ref = oracle.permute(shards.view(torch.int16).numpy(), 4)
+    assert tuple(out.shape) == (4, 1, 4608, 6, 128)
+    assert out.cpu().view(torch.int16).numpy().tobytes() == ref.tobytes()
+    log("  permute [4,1,1152,24,128] -> [4,1,4608,6,128] bit-exact")
+
+
+def test_wan22_5b_full_sequence():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.WAN5B
+    log("workload %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    _check_rows("wan5b", w, o, lse, q, k, v)
+
+
+def test_wan21_14b_ulysses8_share_kv8_merge():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.WAN14B_U8
+    log("workload %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)
+    o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
+    torch.cuda.synchronize()
+    _check_rows("wan14b u8", w, o, lse, q, k, v, n=256)

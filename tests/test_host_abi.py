@@ -1,0 +1,125 @@
+"""CPU-only checks of the C ABI library and the host logic (no GPU work is done).
+
+* libdtl.so loads and exports every function include/dtl.h declares.
+* Invalid arguments are rejected on the host with the documented status codes,
+  before anything is launched (the pointers here are never dereferenced).
+* The kernels' index helpers (multiply-high division, XCD-contiguous workgroup
+  remapping) are checked on the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dtl.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    import diffusion_transformer_long_amd as dtl
+    names = _declared_functions()
+    assert set(names) == set(dtl.EXPORTS), names
+    lib = ctypes.CDLL(dtl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dtl.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(r" T %s$" % n, out, flags=re.M), n
+
+
+def test_status_strings():
+    import diffusion_transformer_long_amd as dtl
+    for code, word in ((0, "OK"), (1, "INVALID"), (2, "UNSUPPORTED"), (3, "HIP")):
+        assert word in dtl.status_string(code)
+    assert "UNKNOWN" in dtl.status_string(99)
+
+
+# Fake, 16-byte aligned, disjoint "device" addresses.  Every call below fails validation,
+# so they are never handed to a kernel.
+A, Bp, C, Dp, E = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _attn(lib, q=A, k=Bp, v=C, o=Dp, lse=E, B=1, Nq=128, Nkv=128, H=2, D=128, scale=0.088, dt=0):
+    return lib.attn_fwd_lse(q, k, v, o, lse, B, Nq, Nkv, H, D, scale, dt, None)
+
+
+def test_attn_fwd_lse_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+    assert _attn(lib, q=None) == INV
+    assert _attn(lib, lse=None) == INV
+    for kw in ({"B": 0}, {"Nq": 0}, {"Nkv": 0}, {"H": -1}, {"D": 0}):
+        assert _attn(lib, **kw) == INV, kw
+    for sc in (0.0, -1.0, float("inf"), float("nan")):
+        assert _attn(lib, scale=sc) == INV, sc
+    assert _attn(lib, q=A + 8) == INV          # misaligned
+    assert _attn(lib, o=A + 64) == INV         # output overlaps q
+    assert _attn(lib, lse=Dp + 16) == INV      # lse overlaps o
+    assert _attn(lib, D=96) == UNS
+    assert _attn(lib, D=256) == UNS
+    assert _attn(lib, dt=7) == UNS
+
+
+def test_attn_merge_lse_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+
+    def m(op=A, lp=Bp, o=C, lse=Dp, P=4, B=1, N=64, H=2, D=128, pd=1, od=0):
+        return lib.attn_merge_lse(op, lp, o, lse, P, B, N, H, D, pd, od, None)
+    assert m(op=None) == INV and m(lp=None) == INV and m(o=None) == INV
+    assert m(P=0) == INV and m(N=0) == INV
+    assert m(o=A + 32) == INV                   # o overlaps the parts
+    assert m(lse=C + 16) == INV                 # lse overlaps o
+    assert m(op=A + 4) == INV
+    assert m(D=12) == UNS and m(pd=5) == UNS and m(od=9) == UNS
+
+
+def test_seq_to_head_permute_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+
+    def pm(i=A, o=Bp, p=4, B=1, N=64, H=8, D=128, eb=2):
+        return lib.seq_to_head_permute(i, o, p, B, N, H, D, eb, None)
+    assert pm(i=None) == INV and pm(o=None) == INV
+    assert pm(N=66) == INV                      # p does not divide N
+    assert pm(H=6) == INV                       # p does not divide H
+    assert pm(p=0) == INV
+    assert pm(o=A + 1024) == INV                # overlap
+    assert pm(i=A + 2) == INV                   # misaligned
+    assert pm(eb=3) == UNS and pm(eb=16) == UNS
+
+
+def test_binding_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    import diffusion_transformer_long_amd as dtl
+    x = torch.zeros((1, 8, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dtl.attn_fwd_lse(x, x, x)
+    with pytest.raises(ValueError):
+        dtl.seq_to_head_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
+
+
+def test_host_index_helpers(tmp_path):
+    src = os.path.join(ROOT, "tests", "host", "host_logic_check.cpp")
+    exe = str(tmp_path / "host_logic_check")
+    csrc = os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc")
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    r = subprocess.run([hipcc, "-O2", "-std=c++17", "-I", csrc, "-I", os.path.join(ROOT, "include"),
+                        "--offload-arch=gfx950", "-x", "hip", src, "-o", exe],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.fail("host check build failed:\n" + r.stderr[-3000:])
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout
+    assert out.stdout.strip().startswith("OK")
