@@ -37,7 +37,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_flux_N4608_H24_D128_pmc.txt")
-ATTN_SRC = os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc", "attn_fwd.hip")
+ATTN_SRCS = [os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc", f)
+             for f in ("attn_fwd.hip", "common.h")]
+
+
+def attn_source_sha256():
+    """Hash of the attention kernel's sources; a counter summary taken on other sources is stale."""
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def err(msg):
@@ -55,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the attention kernel source hash and exit")
     return ap.parse_args()
 
 
@@ -85,7 +96,7 @@ def pmc_traffic():
     if not os.path.exists(PMC_SUMMARY):
         return None
     text = open(PMC_SUMMARY).read()
-    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    sha = attn_source_sha256()
     m = re.search(r"^source_sha256:\s*(\w+)", text, re.M)
     t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
     if not m or not t or m.group(1) != sha:
@@ -128,6 +139,9 @@ def _cpu_model():
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(attn_source_sha256())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

@@ -28,11 +28,16 @@
 //   The O^T accumulator also keeps one query per lane, so the softmax rescale is a
 //   per-lane scalar.
 //
-// Softmax in base 2: p = exp2(s * scale*log2(e) - m), m the running max of the scaled
-// logits in log2 units.  The running max is only moved when some row's tile max
-// exceeds it by more than 8 (the accumulators are then rescaled); otherwise p <= 2^8,
-// which f32 and bf16 hold without overflow.  The result is the same softmax, since
-// numerator and denominator share the reference m.
+// Softmax in base 2: p = exp2(s * scale*log2(e) - m), m a reference max of the scaled
+// logits in log2 units.  The reference is only moved when some row's tile max exceeds
+// it by more than kRescaleThreshold (the accumulators are then rescaled); otherwise
+// p <= 2^threshold, which f32 and bf16 hold without overflow.  The result is the same
+// softmax, since numerator and denominator share the reference m.
+//
+// Full key tiles load without bounds checks from a uniform tile base plus per-thread
+// offsets fixed for the whole loop; only the ragged last tile is predicated and masked.
+#include <type_traits>
+
 #include "common.h"
 
 namespace dtl {
@@ -42,7 +47,16 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;   // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per iteration
-constexpr float kRescaleThreshold = 8.0f;
+// The running max moves only when a tile raises it by more than this (log2 units).
+// A larger threshold skips more accumulator rescales, but then the dominant weight of a
+// peaked row is exp2(x) with x in (0, threshold] instead of exactly 1, and its bf16
+// rounding no longer cancels: at FLUX-like logits (std 3) a threshold of 8 roughly
+// triples the worst-case error of the f32 result.  2 keeps it within 2x of the exact-max
+// scheme while rescaling about a third of the tiles at N=4608 and 3% at N=27280.
+#ifndef DTL_RESCALE_THRESHOLD
+#define DTL_RESCALE_THRESHOLD 2.0f
+#endif
+constexpr float kRescaleThreshold = DTL_RESCALE_THRESHOLD;
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -59,6 +73,17 @@ struct Tile {
 // LDS row of key `key` of a tile: bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int krow_slot(int key) {
     return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// max over the two lane halves (lanes l and l^32 hold the two halves of one query row)
+__device__ __forceinline__ float halves_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 template <int D, bool OUT_F32>
@@ -83,7 +108,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int h = bh % H;
     const int b = bh / H;
 
-    const long tok_stride = (long)H * D;
+    const int tok_stride = H * D;  // elements between consecutive tokens (H*D <= 2^24, checked on the host)
     const uint16_t* kbase = k + ((long)b * Nkv * H + h) * D;
     const uint16_t* vbase = v + ((long)b * Nkv * H + h) * D;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -100,57 +125,69 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         }
     }
 
-    u32x4 kreg[T::kChunks];
-    u32x4 vreg[T::vPerThread][4];
+    // Per-thread tile geometry, fixed for the whole loop.
+    //   K: chunk c covers key row k_row[c] and 8 columns; it lands in LDS row krow_slot(k_row[c]).
+    //   V: a block of 4 keys (vk0..vk0+3) x 8 columns (vd0..vd0+7), stored transposed.
+    int k_goff[T::kChunks], k_soff[T::kChunks], k_row[T::kChunks];
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c) {
+        const int idx = tid + c * kThreads;
+        const int row = idx / (D / 8), col = idx % (D / 8);
+        k_row[c] = row;
+        k_goff[c] = row * tok_stride + col * 8;
+        k_soff[c] = krow_slot(row) * T::kRow + col * 8;
+    }
+    const bool v_active = T::vBlocks >= kThreads || tid < T::vBlocks;
+    const int vk0 = (tid % (kBlockN / 4)) * 4;
+    const int vd0 = (tid / (kBlockN / 4)) * 8;
+    const int v_goff = vk0 * tok_stride + vd0;
+    const int v_soff = vd0 * T::vRow + vk0;
+    static_assert(T::vPerThread == 1, "one V block per thread");
 
-    auto load_tile = [&](int kv0) {
+    u32x4 kreg[T::kChunks];
+    u32x4 vreg[4];
+
+    // Global -> registers for the tile starting at key kv0.  A full tile needs no checks;
+    // the ragged last tile reads zeros past Nkv (its logits are masked below).
+    auto load_full = [&](int kv0) {
+        const uint16_t* kt = kbase + (long)kv0 * tok_stride;
+        const uint16_t* vt = vbase + (long)kv0 * tok_stride;
 #pragma unroll
-        for (int c = 0; c < T::kChunks; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / (D / 8), col = idx % (D / 8);
-            const int key = kv0 + row;
-            kreg[c] = key < Nkv
-                ? *reinterpret_cast<const u32x4*>(kbase + (long)key * tok_stride + col * 8)
-                : zero4;
+        for (int c = 0; c < T::kChunks; ++c)
+            kreg[c] = *reinterpret_cast<const u32x4*>(kt + k_goff[c]);
+        if (v_active) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                vreg[j] = *reinterpret_cast<const u32x4*>(vt + v_goff + j * tok_stride);
         }
+    };
+    auto load_partial = [&](int kv0) {
+        const uint16_t* kt = kbase + (long)kv0 * tok_stride;
+        const uint16_t* vt = vbase + (long)kv0 * tok_stride;
+        const int nk = Nkv - kv0;
 #pragma unroll
-        for (int c = 0; c < T::vPerThread; ++c) {
-            const int blk = tid + c * kThreads;
-            if (blk < T::vBlocks) {
-                const int kg = blk % (kBlockN / 4), dg = blk / (kBlockN / 4);
+        for (int c = 0; c < T::kChunks; ++c)
+            kreg[c] = k_row[c] < nk ? *reinterpret_cast<const u32x4*>(kt + k_goff[c]) : zero4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = kv0 + kg * 4 + j;
-                    vreg[c][j] = key < Nkv
-                        ? *reinterpret_cast<const u32x4*>(vbase + (long)key * tok_stride + dg * 8)
-                        : zero4;
-                }
-            }
-        }
+        for (int j = 0; j < 4; ++j)
+            vreg[j] = (v_active && vk0 + j < nk)
+                ? *reinterpret_cast<const u32x4*>(vt + v_goff + j * tok_stride) : zero4;
     };
 
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int c = 0; c < T::kChunks; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / (D / 8), col = idx % (D / 8);
-            *reinterpret_cast<u32x4*>(&sK[buf][krow_slot(row) * T::kRow + col * 8]) = kreg[c];
-        }
+        for (int c = 0; c < T::kChunks; ++c)
+            *reinterpret_cast<u32x4*>(&sK[buf][k_soff[c]]) = kreg[c];
+        if (v_active) {
 #pragma unroll
-        for (int c = 0; c < T::vPerThread; ++c) {
-            const int blk = tid + c * kThreads;
-            if (blk < T::vBlocks) {
-                const int kg = blk % (kBlockN / 4), dg = blk / (kBlockN / 4);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t a0 = vreg[c][0][w], a1 = vreg[c][1][w];
-                    const uint32_t a2 = vreg[c][2][w], a3 = vreg[c][3][w];
-                    // column 2w of the 8: the low halves of the 4 keys; column 2w+1: the high halves
-                    u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                    u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-                    *reinterpret_cast<u32x2*>(&sV[buf][(dg * 8 + 2 * w) * T::vRow + kg * 4]) = lo;
-                    *reinterpret_cast<u32x2*>(&sV[buf][(dg * 8 + 2 * w + 1) * T::vRow + kg * 4]) = hi;
-                }
+            for (int w = 0; w < 4; ++w) {
+                // column vd0+2w: low halves of the 4 keys; column vd0+2w+1: high halves
+                u32x2 lo = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u),
+                            __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
+                u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
+                            __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
+                *reinterpret_cast<u32x2*>(&sV[buf][v_soff + (2 * w) * T::vRow]) = lo;
+                *reinterpret_cast<u32x2*>(&sV[buf][v_soff + (2 * w + 1) * T::vRow]) = hi;
             }
         }
     };
@@ -163,21 +200,19 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     float m_run = -INFINITY;  // reference max of this lane's query row (log2 units)
     float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
 
-    const int n_tiles = (Nkv + kBlockN - 1) / kBlockN;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
+    // One key tile: S^T, online softmax, O^T update; meanwhile the next tile is fetched
+    // (PF: 0 none, 1 a full tile, 2 the ragged last tile) and staged into the other buffer.
+    auto step = [&](auto pf_c, auto mask_c, int it) {
+        constexpr int PF = decltype(pf_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value;
         const int buf = it & 1;
         const int kv0 = it * kBlockN;
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next) load_tile(kv0 + kBlockN);
+        if constexpr (PF == 1) load_full(kv0 + kBlockN);
+        if constexpr (PF == 2) load_partial(kv0 + kBlockN);
 
         const uint16_t* sk = sK[buf];
         const uint16_t* sv = sV[buf];
 
-        // S^T for two 32-key blocks.
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -190,7 +225,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
         }
 
-        if (kv0 + kBlockN > Nkv) {  // ragged last tile: keys past the end get weight 0
+        if constexpr (MASK) {  // keys past the end get weight 0
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -205,8 +240,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mx2 = mx * scale_log2;
+        const float mx2 = halves_max(mx) * scale_log2;
         if (__any(mx2 > m_run + kRescaleThreshold)) {
             const float m_new = fmaxf(m_run, mx2);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -245,11 +279,30 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hf], acc[db], 0, 0, 0);
                 }
 
-        if (has_next) store_tile(buf ^ 1);
+        if constexpr (PF != 0) store_tile(buf ^ 1);
         __syncthreads();
-    }
+    };
+    using PF0 = std::integral_constant<int, 0>;
+    using PF1 = std::integral_constant<int, 1>;
+    using PF2 = std::integral_constant<int, 2>;
+    using NOMASK = std::integral_constant<bool, false>;
+    using MASKED = std::integral_constant<bool, true>;
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const int n_full = Nkv / kBlockN;          // tiles without a ragged tail
+    const bool has_tail = Nkv % kBlockN != 0;  // one ragged tile after them
+    if (n_full > 0) load_full(0); else load_partial(0);
+    store_tile(0);
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < n_full; ++it) step(PF1{}, NOMASK{}, it);
+    if (n_full > 0) {
+        if (has_tail) step(PF2{}, NOMASK{}, it);
+        else step(PF0{}, NOMASK{}, it);
+        ++it;
+    }
+    if (has_tail) step(PF0{}, MASKED{}, it);
+
+    const float l_tot = halves_sum(l_run);
     if (qrow < Nq) {
         const float inv = 1.0f / l_tot;
         const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;

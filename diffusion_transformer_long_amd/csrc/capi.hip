@@ -52,7 +52,8 @@ dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, fl
         overlap(lse, l_bytes, v, kv_bytes))
         return DTL_ERR_INVALID_ARG;
     const long tiles = ((long)Nq + 127) / 128 * H * B;
-    if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)B * Nq * H > kIntMax)
+    if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)B * Nq * H > kIntMax ||
+        (long)H * D > (1l << 24))
         return DTL_ERR_INVALID_ARG;
     hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, B, Nq, Nkv, H, D, softmax_scale,
                                         o_dtype == DTL_F32, stream);
@@ -66,7 +67,7 @@ dtl_status attn_merge_lse(const void* o_parts, const float* lse_parts, void* o, 
     if (P <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || (lse && !aligned16(lse)))
         return DTL_ERR_INVALID_ARG;
-    if (D % 8 != 0) return DTL_ERR_UNSUPPORTED;
+    if (D % 8 != 0 || P > dtl::merge_max_parts()) return DTL_ERR_UNSUPPORTED;
     if ((parts_dtype != DTL_BF16 && parts_dtype != DTL_F32) ||
         (out_dtype != DTL_BF16 && out_dtype != DTL_F32))
         return DTL_ERR_UNSUPPORTED;

@@ -5,10 +5,14 @@
 // multi-GPU diffusion parallelism, section 4.2; MindIE SD "多卡并行" page, Ring
 // Sequence Parallel section).
 //
-// One thread owns 8 consecutive head_dim values of one row and streams them from
-// all P parts (32 B per part in f32), so a wave reads whole 1 KB segments per part.
-// Row weights are computed per thread from the P lse values, which every thread of
-// the row loads from the same addresses (one cache line, broadcast).
+// A workgroup owns kRows consecutive output rows (row = (b*N + n)*H + h).
+//   phase 1: one thread per (row, part) loads lse_t into LDS;
+//   phase 2: one thread per row turns them into L and the P weights exp(lse_t - L)
+//            (0 for an empty part), kept in LDS;
+//   phase 3: every thread streams 16-byte vectors of the rows from all P parts — all
+//            P loads issued before the first use, consecutive threads on consecutive
+//            16 B, so each wave reads whole 1 KB segments — and accumulates w_t * o_t.
+// The weights are computed once per row instead of once per thread.
 #include "common.h"
 #include "fastdiv.h"
 
@@ -16,89 +20,131 @@ namespace dtl {
 namespace {
 
 constexpr int kThreads = 256;
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_ __attribute__((ext_vector_type(8)));
+constexpr int kRows = 16;
+constexpr int kMaxParts = 256;
+typedef __bf16 bf16x4_ __attribute__((ext_vector_type(4)));
 
 template <bool PARTS_F32>
-__device__ __forceinline__ f32x8 load8(const void* base, long off) {
+__device__ __forceinline__ f32x4 load4(const void* base, long off) {
     if constexpr (PARTS_F32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
-        f32x4 a = __builtin_nontemporal_load(p);
-        f32x4 b = __builtin_nontemporal_load(p + 1);
-        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off));
     } else {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
-        u32x4 a = __builtin_nontemporal_load(p);
-        return __builtin_convertvector(__builtin_bit_cast(bf16x8_, a), f32x8);
+        const u32x2 a = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + off));
+        return __builtin_convertvector(__builtin_bit_cast(bf16x4_, a), f32x4);
     }
 }
 
 template <bool PARTS_F32, bool OUT_F32>
 __global__ __launch_bounds__(kThreads)
 void merge_kernel(const void* __restrict__ o_parts, const float* __restrict__ lse_parts,
-                  void* __restrict__ o, float* __restrict__ lse, int P, FastDiv div_vpr,
-                  FastDiv div_h, FastDiv div_n, uint32_t total_vec, long part_o, long part_l, int D) {
-    const uint32_t e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= total_vec) return;
-    const uint32_t row = div_vpr.div(e);          // (b*N + n)*H + h
-    const uint32_t c = e - row * div_vpr.d;       // which 8-value group of the row
-    const uint32_t bn = div_h.div(row);
-    const uint32_t hh = row - bn * div_h.d;
-    const uint32_t b = div_n.div(bn);
-    const uint32_t n = bn - b * div_n.d;
-    const long li = ((long)b * div_h.d + hh) * div_n.d + n;   // [B, H, N] index
-    const long off = (long)row * D + c * 8;
+                  void* __restrict__ o, float* __restrict__ lse, int P, uint32_t rows,
+                  FastDiv div_h, FastDiv div_n, FastDiv div_vpr, long part_o, long part_l) {
+    extern __shared__ float smem[];   // [kRows][P] lse values, then [kRows][P] weights
+    float* s_lse = smem;
+    float* s_w = smem + kRows * P;
 
-    float M = -INFINITY;
-    for (int t = 0; t < P; ++t) M = fmaxf(M, lse_parts[t * part_l + li]);
+    const uint32_t row0 = blockIdx.x * kRows;
+    const int nrows = (int)min((uint32_t)kRows, rows - row0);
+    const int tid = threadIdx.x;
 
-    f32x8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = -INFINITY;
-    if (M != -INFINITY) {
-        float sum = 0.f;
-        for (int t = 0; t < P; ++t) sum += __expf(lse_parts[t * part_l + li] - M);
-        L = M + __logf(sum);
-        for (int t = 0; t < P; ++t) {
-            const float lt = lse_parts[t * part_l + li];
-            if (lt == -INFINITY) continue;   // an empty part adds nothing
-            const float w = __expf(lt - L);
-            acc += w * load8<PARTS_F32>(o_parts, t * part_o + off);
+    // [B, H, N] index of a row
+    auto lse_index = [&](uint32_t row) -> long {
+        const uint32_t bn = div_h.div(row);
+        const uint32_t hh = row - bn * div_h.d;
+        const uint32_t b = div_n.div(bn);
+        const uint32_t n = bn - b * div_n.d;
+        return ((long)b * div_h.d + hh) * div_n.d + n;
+    };
+
+    for (int e = tid; e < nrows * P; e += kThreads) {
+        const int rr = e / P, t = e - rr * P;
+        s_lse[rr * P + t] = lse_parts[t * part_l + lse_index(row0 + rr)];
+    }
+    __syncthreads();
+
+    if (tid < nrows) {
+        const float* l = s_lse + tid * P;
+        float M = -INFINITY;
+        for (int t = 0; t < P; ++t) M = fmaxf(M, l[t]);
+        float* w = s_w + tid * P;
+        float L = -INFINITY;
+        if (M == -INFINITY) {
+            for (int t = 0; t < P; ++t) w[t] = 0.f;
+        } else {
+            float sum = 0.f;
+            for (int t = 0; t < P; ++t) {
+                const float e = __expf(l[t] - M);   // 0 for an empty part
+                w[t] = e;
+                sum += e;
+            }
+            const float inv = 1.0f / sum;
+            for (int t = 0; t < P; ++t) w[t] *= inv;
+            L = M + __logf(sum);
+        }
+        if (lse != nullptr) lse[lse_index(row0 + tid)] = L;
+    }
+    __syncthreads();
+
+    const uint32_t vpr = div_vpr.d;                 // 16-byte vectors per row
+    const uint32_t nvec = (uint32_t)nrows * vpr;
+    const long base = (long)row0 * vpr * 4;         // element offset of the block's first row
+    for (uint32_t e = tid; e < nvec; e += kThreads) {
+        const uint32_t rr = div_vpr.div(e);
+        const long off = base + (long)e * 4;
+        const float* w = s_w + rr * P;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int t = 0;
+        for (; t + 4 <= P; t += 4) {
+            f32x4 x0 = load4<PARTS_F32>(o_parts, (t + 0) * part_o + off);
+            f32x4 x1 = load4<PARTS_F32>(o_parts, (t + 1) * part_o + off);
+            f32x4 x2 = load4<PARTS_F32>(o_parts, (t + 2) * part_o + off);
+            f32x4 x3 = load4<PARTS_F32>(o_parts, (t + 3) * part_o + off);
+            // an empty part has weight 0 and may hold anything (even NaN): select, not multiply
+            if (w[t + 0] != 0.f) acc += w[t + 0] * x0;
+            if (w[t + 1] != 0.f) acc += w[t + 1] * x1;
+            if (w[t + 2] != 0.f) acc += w[t + 2] * x2;
+            if (w[t + 3] != 0.f) acc += w[t + 3] * x3;
+        }
+        for (; t < P; ++t) {
+            f32x4 x = load4<PARTS_F32>(o_parts, t * part_o + off);
+            if (w[t] != 0.f) acc += w[t] * x;
+        }
+        if constexpr (OUT_F32) {
+            __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(static_cast<float*>(o) + off));
+        } else {
+            const bf16x4_ y = __builtin_convertvector(acc, bf16x4_);
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x2, y),
+                                        reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + off));
         }
     }
-    if constexpr (OUT_F32) {
-        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(o) + off);
-        __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, p);
-        __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, p + 1);
-    } else {
-        bf16x8_ x = __builtin_convertvector(acc, bf16x8_);
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x),
-                                    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o) + off));
-    }
-    if (lse != nullptr && c == 0) lse[li] = L;
 }
 
 }  // namespace
 
+int merge_max_parts() { return kMaxParts; }
+
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
                         int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,
                         hipStream_t stream) {
-    const long rows = (long)B * N * H;
-    const uint32_t vpr = (uint32_t)(D / 8);
-    const uint32_t total_vec = (uint32_t)(rows * vpr);  // the caller has checked < 2^31
-    const long part_o = rows * D;
-    const long part_l = rows;
-    const FastDiv dv = FastDiv::make(vpr), dh = FastDiv::make((uint32_t)H), dn = FastDiv::make((uint32_t)N);
-    const dim3 grid((total_vec + kThreads - 1) / kThreads), block(kThreads);
+    const uint32_t rows = (uint32_t)((long)B * N * H);  // the caller has checked < 2^31
+    const long part_o = (long)rows * D;
+    const long part_l = (long)rows;
+    const FastDiv dh = FastDiv::make((uint32_t)H), dn = FastDiv::make((uint32_t)N);
+    const FastDiv dv = FastDiv::make((uint32_t)(D / 4));
+    const dim3 grid((rows + kRows - 1) / kRows), block(kThreads);
+    const size_t shmem = sizeof(float) * 2 * kRows * P;
     if (parts_f32) {
         if (out_f32)
-            merge_kernel<true, true><<<grid, block, 0, stream>>>(o_parts, lse_parts, o, lse, P, dv, dh, dn, total_vec, part_o, part_l, D);
+            merge_kernel<true, true><<<grid, block, shmem, stream>>>(o_parts, lse_parts, o, lse, P, rows, dh, dn, dv, part_o, part_l);
         else
-            merge_kernel<true, false><<<grid, block, 0, stream>>>(o_parts, lse_parts, o, lse, P, dv, dh, dn, total_vec, part_o, part_l, D);
+            merge_kernel<true, false><<<grid, block, shmem, stream>>>(o_parts, lse_parts, o, lse, P, rows, dh, dn, dv, part_o, part_l);
     } else {
         if (out_f32)
-            merge_kernel<false, true><<<grid, block, 0, stream>>>(o_parts, lse_parts, o, lse, P, dv, dh, dn, total_vec, part_o, part_l, D);
+            merge_kernel<false, true><<<grid, block, shmem, stream>>>(o_parts, lse_parts, o, lse, P, rows, dh, dn, dv, part_o, part_l);
         else
-            merge_kernel<false, false><<<grid, block, 0, stream>>>(o_parts, lse_parts, o, lse, P, dv, dh, dn, total_vec, part_o, part_l, D);
+            merge_kernel<false, false><<<grid, block, shmem, stream>>>(o_parts, lse_parts, o, lse, P, rows, dh, dn, dv, part_o, part_l);
     }
     return hipGetLastError();
 }

@@ -92,8 +92,8 @@ dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
  *   lse        f32 [B, H, N], or NULL to skip writing it
  *
  * Errors: DTL_ERR_INVALID_ARG for null inputs or o, sizes <= 0, misalignment, or an
- * output overlapping an input; DTL_ERR_UNSUPPORTED for D not a multiple of 8 or a
- * dtype outside {DTL_BF16, DTL_F32}.
+ * output overlapping an input; DTL_ERR_UNSUPPORTED for D not a multiple of 8, P > 256,
+ * or a dtype outside {DTL_BF16, DTL_F32}.
  */
 dtl_status attn_merge_lse(const void *o_parts, const float *lse_parts,
                           void *o, float *lse,

@@ -21,7 +21,7 @@ from gpu_helpers import assert_close, log, to_np
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-SAMPLE_ROWS = 384
+SAMPLE_ROWS = 2048
 
 
 def _check_rows(name, w, o, lse, q, k, v, n=SAMPLE_ROWS, seed=0):
@@ -57,7 +57,7 @@ def test_flux_full_sequence():
     q, k, v = synthetic.workload_qkv(w)
     o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
-    _check_rows("flux", w, o, lse, q, k, v, n=1024)
+    _check_rows("flux", w, o, lse, q, k, v, n=8192)
 
 
 def test_flux_ring4_share_and_ulysses4_permute():
@@ -70,7 +70,7 @@ def test_flux_ring4_share_and_ulysses4_permute():
         q = qf[:, rank * w.Nq:(rank + 1) * w.Nq].contiguous()
         o, lse = dtl.ring_attention(q.to(DEV), kd, vd, w.chunks)
         torch.cuda.synchronize()
-        _check_rows("ring4 rank%d" % rank, w, o, lse, q, k, v, n=256, seed=300 + rank)
+        _check_rows("ring4 rank%d" % rank, w, o, lse, q, k, v, n=1024, seed=300 + rank)
     shards = qf.reshape(1, 4, w.Nq, w.H, w.D).transpose(0, 1).contiguous()   # [4,1,1152,24,128]
     out = dtl.seq_to_head_permute(shards.to(DEV), 4)
     torch.cuda.synchronize()
@@ -97,4 +97,4 @@ def test_wan21_14b_ulysses8_share_kv8_merge():
     q, k, v = synthetic.workload_qkv(w)
     o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
     torch.cuda.synchronize()
-    _check_rows("wan14b u8", w, o, lse, q, k, v, n=256)
+    _check_rows("wan14b u8", w, o, lse, q, k, v, n=1024)

@@ -81,7 +81,7 @@ def test_attn_merge_lse_validation():
     assert m(o=A + 32) == INV                   # o overlaps the parts
     assert m(lse=C + 16) == INV                 # lse overlaps o
     assert m(op=A + 4) == INV
-    assert m(D=12) == UNS and m(pd=5) == UNS and m(od=9) == UNS
+    assert m(D=12) == UNS and m(pd=5) == UNS and m(od=9) == UNS and m(P=257) == UNS
 
 
 def test_seq_to_head_permute_validation():
