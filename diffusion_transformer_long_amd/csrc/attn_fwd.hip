@@ -29,10 +29,18 @@
 //   per-lane scalar.
 //
 // Softmax in base 2: p = exp2(s * scale*log2(e) - m), m a reference max of the scaled
-// logits in log2 units.  The reference is only moved when some row's tile max exceeds
-// it by more than kRescaleThreshold (the accumulators are then rescaled); otherwise
-// p <= 2^threshold, which f32 and bf16 hold without overflow.  The result is the same
+// logits in log2 units, updated once per 32-key half.  The reference is only moved when
+// some row's half-tile max exceeds it by more than kRescaleThreshold (the accumulators
+// are then rescaled); otherwise p <= 2^threshold, which f32 and bf16 hold without
+// overflow.  The row sum is taken over the bf16-rounded weights (two per v_dot2 against
+// (1, 1)), i.e. over exactly the weights the P.V product uses.  The result is the same
 // softmax, since numerator and denominator share the reference m.
+//
+// Each key tile runs as four blocks that pair MFMAs with VALU work independent of them
+// (S of key half 0; S of half 1 with the softmax of half 0; P.V of half 0 with the
+// softmax of half 1; P.V of half 1 with the V transpose and the LDS stores of the next
+// tile), since a wave issues in order and VALU work only overlaps an MFMA when it sits
+// between MFMAs in the instruction stream.
 //
 // Full key tiles load without bounds checks from a uniform tile base plus per-thread
 // offsets fixed for the whole loop; only the ragged last tile is predicated and masked.
@@ -47,12 +55,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;   // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per iteration
-// The running max moves only when a tile raises it by more than this (log2 units).
+// The running max moves only when a tile half raises it by more than this (log2 units).
 // A larger threshold skips more accumulator rescales, but then the dominant weight of a
-// peaked row is exp2(x) with x in (0, threshold] instead of exactly 1, and its bf16
-// rounding no longer cancels: at FLUX-like logits (std 3) a threshold of 8 roughly
-// triples the worst-case error of the f32 result.  2 keeps it within 2x of the exact-max
-// scheme while rescaling about a third of the tiles at N=4608 and 3% at N=27280.
+// peaked row is exp2(x) with x in (0, threshold] instead of exactly 1; at FLUX-like
+// logits (std 3) a threshold of 8 with an f32 row sum roughly triples the worst-case
+// error.  2 keeps the error near that of the exact-max scheme while rescaling about a
+// third of the tiles at N=4608 and 3% at N=27280.
 #ifndef DTL_RESCALE_THRESHOLD
 #define DTL_RESCALE_THRESHOLD 2.0f
 #endif
@@ -200,8 +208,72 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     float m_run = -INFINITY;  // reference max of this lane's query row (log2 units)
     float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
 
-    // One key tile: S^T, online softmax, O^T update; meanwhile the next tile is fetched
-    // (PF: 0 none, 1 a full tile, 2 the ragged last tile) and staged into the other buffer.
+    // Online-softmax update for one 32-key half of a tile: moves the reference max when the
+    // half raises it by more than kRescaleThreshold, then rounds exp2(s*c - m) to bf16 for the
+    // P.V product and returns the f32 sum of this lane's 16 rounded weights.  Returns whether the
+    // accumulators need the rescale by alpha (wave-uniform).
+    auto softmax_half = [&](const f32x16& s, bf16x8 (&pf)[2], float& lsum, float& alpha) -> bool {
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        const float mx2 = halves_max(mx) * scale_log2;
+        const bool rescale = __any(mx2 > m_run + kRescaleThreshold);
+        const float m_new = rescale ? fmaxf(m_run, mx2) : m_run;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 when unchanged
+        m_run = m_new;
+        l_run *= alpha;
+        lsum = 0.f;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            f32x8 e;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                e[i] = __builtin_amdgcn_exp2f(fmaf(s[hf * 8 + i], scale_log2, -m_run));
+            pf[hf] = __builtin_convertvector(e, bf16x8);
+            // the row sum is taken over the rounded weights, two per v_dot2 against (1, 1):
+            // numerator (P.V on the bf16 P) and denominator then round the same way
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 0, 1), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 2, 3), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 4, 5), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 6, 7), ones, lsum, false);
+        }
+        return rescale;
+    };
+    auto rescale_acc = [&](float alpha) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    };
+    auto s_half = [&](f32x16& s, const uint16_t* sk, int kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + r) * T::kRow + ks * 16 + g * 8);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+        }
+    };
+    auto pv_half = [&](const bf16x8 (&pf)[2], const uint16_t* sv, int kb) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    sv + (db * 32 + r) * T::vRow + kb * 32 + hf * 16 + g * 8);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[hf], acc[db], 0, 0, 0);
+            }
+    };
+
+    // One key tile, as four blocks that each pair MFMAs with VALU work independent of them,
+    // so a wave keeps its softmax under its own MFMAs:
+    //   S of key half 0
+    //   S of key half 1            with  the softmax of half 0
+    //   P.V of half 0              with  the softmax of half 1
+    //   P.V of half 1              with  the V transpose and LDS stores of the next tile
+    // Meanwhile the next tile is fetched (PF: 0 none, 1 a full tile, 2 the ragged last
+    // tile) and staged into the other buffer.
     auto step = [&](auto pf_c, auto mask_c, int it) {
         constexpr int PF = decltype(pf_c)::value;
         constexpr bool MASK = decltype(mask_c)::value;
@@ -212,73 +284,38 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
         const uint16_t* sk = sK[buf];
         const uint16_t* sv = sV[buf];
+        f32x16 s0, s1;
+        bf16x8 p0[2], p1[2];
+        float ls0, ls1, a0, a1;
 
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + r) * T::kRow + ks * 16 + g * 8);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-            }
-        }
-
+        s_half(s0, sk, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        s_half(s1, sk, 1);
         if constexpr (MASK) {  // keys past the end get weight 0
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kv0 + kb * 32 + 16 * (i / 8) + 8 * g + (i % 8);
-                    if (key >= Nkv) s[kb][i] = -INFINITY;
-                }
-        }
-
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        const float mx2 = halves_max(mx) * scale_log2;
-        if (__any(mx2 > m_run + kRescaleThreshold)) {
-            const float m_new = fmaxf(m_run, mx2);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-            m_run = m_new;
-        }
-
-        bf16x8 pf[2][2];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x8 e;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][hf * 8 + i], scale_log2, -m_run));
-                    lsum += e[i];
-                }
-                pf[kb][hf] = __builtin_convertvector(e, bf16x8);
+            for (int i = 0; i < 16; ++i) {
+                const int key = kv0 + 16 * (i / 8) + 8 * g + (i % 8);
+                if (key >= Nkv) s0[i] = -INFINITY;
             }
-        l_run += lsum;
-
+        }
+        const bool r0 = softmax_half(s0, p0, ls0, a0);
+        asm volatile("" : "+v"(p0[0]), "+v"(p0[1]), "+v"(ls0));   // keep it in this block
+        __builtin_amdgcn_sched_barrier(0);
+        if (r0) rescale_acc(a0);
+        pv_half(p0, sv, 0);
+        if constexpr (MASK) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        sv + (db * 32 + r) * T::vRow + kb * 32 + hf * 16 + g * 8);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hf], acc[db], 0, 0, 0);
-                }
-
+            for (int i = 0; i < 16; ++i) {
+                const int key = kv0 + 32 + 16 * (i / 8) + 8 * g + (i % 8);
+                if (key >= Nkv) s1[i] = -INFINITY;
+            }
+        }
+        const bool r1 = softmax_half(s1, p1, ls1, a1);
+        asm volatile("" : "+v"(p1[0]), "+v"(p1[1]), "+v"(ls1));
+        __builtin_amdgcn_sched_barrier(0);
+        l_run += ls0 * a1 + ls1;
+        if (r1) rescale_acc(a1);
+        pv_half(p1, sv, 1);
         if constexpr (PF != 0) store_tile(buf ^ 1);
         __syncthreads();
     };
