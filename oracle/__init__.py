@@ -14,6 +14,11 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   merge           : Ring equivalence against attn, decimal brute force, invariants.
   permute         : numpy reshape/transpose, an emulation of the split / exchange
                     / concatenate sequence, round trip, the pages' byte counts.
+  head_to_seq     : an emulation of the split-by-tokens / exchange / concatenate-
+                    along-heads sequence, numpy reshape/transpose, round trips with
+                    permute in both orders.
+  qkv_permute     : the exchange emulation on a packed [.., 3, H, D] tensor, and
+                    per-tensor agreement with permute on the q, k, v slices.
 """
 from __future__ import annotations
 
@@ -47,6 +52,10 @@ class Api:
         lib.oracle_merge.restype = i
         lib.oracle_permute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i, i, i, i, i, i]
         lib.oracle_permute.restype = i
+        lib.oracle_head_to_seq.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i, i, i, i, i, i]
+        lib.oracle_head_to_seq.restype = i
+        lib.oracle_qkv_seq_to_head.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i, i, i, i, i, i]
+        lib.oracle_qkv_seq_to_head.restype = i
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i
         self.lib = lib
@@ -118,6 +127,37 @@ class Api:
             raise ValueError("oracle_permute: bad sizes")
         return out
 
+    def head_to_seq(self, x: np.ndarray, p: int) -> np.ndarray:
+        """Ulysses head->seq permute of stacked head shards: [p,B,N,H/p,D] ->
+        [p,B,N/p,H,D].  Any dtype; a byte-exact copy."""
+        x = np.ascontiguousarray(x)
+        P_, B, N, Hs, D = x.shape
+        assert P_ == p
+        if N % p != 0:
+            raise ValueError("p must divide N")
+        out = np.empty((p, B, N // p, Hs * p, D), dtype=x.dtype)
+        rc = self.lib.oracle_head_to_seq(x.ctypes.data, out.ctypes.data, p, B, N, Hs * p, D,
+                                         x.dtype.itemsize)
+        if rc != 0:
+            raise ValueError("oracle_head_to_seq: bad sizes")
+        return out
+
+    def qkv_permute(self, x: np.ndarray, p: int) -> np.ndarray:
+        """Fused QKV seq->head permute: [p,B,N/p,3,H,D] -> [p,3,B,N,H/p,D].  Any dtype;
+        a byte-exact copy."""
+        x = np.ascontiguousarray(x)
+        P_, B, Ns, three, H, D = x.shape
+        assert P_ == p and three == 3
+        N = Ns * p
+        if H % p != 0:
+            raise ValueError("p must divide H")
+        out = np.empty((p, 3, B, N, H // p, D), dtype=x.dtype)
+        rc = self.lib.oracle_qkv_seq_to_head(x.ctypes.data, out.ctypes.data, p, B, N, H, D,
+                                             x.dtype.itemsize)
+        if rc != 0:
+            raise ValueError("oracle_qkv_seq_to_head: bad sizes")
+        return out
+
 
 def _f64(x) -> np.ndarray:
     """Accept numpy arrays or torch tensors (any float dtype); exact upcast to float64."""
@@ -175,3 +215,11 @@ def merge(o_parts, lse_parts):
 
 def permute(x, p: int):
     return api().permute(x, p)
+
+
+def head_to_seq(x, p: int):
+    return api().head_to_seq(x, p)
+
+
+def qkv_permute(x, p: int):
+    return api().qkv_permute(x, p)

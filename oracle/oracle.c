@@ -24,10 +24,21 @@
  *    (arganzheng.life section 4.1 figure; MindIE SD page, Ulysses section usage
  *    example: split heads into p groups, exchange, concatenate along tokens in
  *    rank order).
+ *  - Ulysses head->seq permute: the all-to-all after attention that turns the
+ *    output back into "N/p tokens x all heads" (arganzheng.life section 4.1 figure,
+ *    the O all-to-all; MindIE SD page, Ulysses usage example: split the attention
+ *    output into p token ranges, exchange, concatenate along heads in rank order).
+ *  - fused QKV seq->head permute: Q, K and V moved by one all-to-all ("AIGC
+ *    分布式推理" CP section: one fused QKV all-to-all plus one for the output per
+ *    self-attention).  Reading: each token's row holds its q, k and v of all heads
+ *    side by side, as a fused QKV projection writes them, and each head group
+ *    receives three separate BSND tensors.
  *
  * Layouts (dense, row-major):  q [B,Nq,H,D], k/v [B,Nkv,H,D], o [B,Nq,H,D],
  * lse [B,H,Nq].  Merge parts: o_parts [P,B,N,H,D], lse_parts [P,B,H,N].
  * Permute: in [p,B,N/p,H,D] -> out [p,B,N,H/p,D].
+ * Inverse permute: in [p,B,N,H/p,D] -> out [p,B,N/p,H,D].
+ * Fused QKV permute: in [p,B,N/p,3,H,D] -> out [p,3,B,N,H/p,D].
  */
 #include <math.h>
 #include <stdint.h>
@@ -206,5 +217,59 @@ int oracle_permute(const void *in, void *out, int p, int B, int N, int H, int D,
                             memcpy(dst + di * elem_bytes, src + si * elem_bytes,
                                    (size_t)elem_bytes);
                         }
+    return 0;
+}
+
+/* Ulysses head->seq permute (after attention), element by element:
+ *   out[s][b][n][j*(H/p) + hh][d] = in[j][b][s*(N/p) + n][hh][d]
+ * for head group j (the rank that computed those heads) and token shard s. */
+int oracle_head_to_seq(const void *in, void *out, int p, int B, int N, int H, int D,
+                       int elem_bytes)
+{
+    if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0 || elem_bytes <= 0)
+        return -1;
+    if (N % p != 0 || H % p != 0)
+        return -1;
+    const unsigned char *src = (const unsigned char *)in;
+    unsigned char *dst = (unsigned char *)out;
+    long Ns = N / p, Hs = H / p;
+    for (long s = 0; s < p; ++s)
+        for (long j = 0; j < p; ++j)
+            for (long b = 0; b < B; ++b)
+                for (long n = 0; n < Ns; ++n)
+                    for (long hh = 0; hh < Hs; ++hh)
+                        for (long d = 0; d < D; ++d) {
+                            long si = (((j * B + b) * (long)N + (s * Ns + n)) * Hs + hh) * D + d;
+                            long di = (((s * B + b) * Ns + n) * H + (j * Hs + hh)) * D + d;
+                            memcpy(dst + di * elem_bytes, src + si * elem_bytes,
+                                   (size_t)elem_bytes);
+                        }
+    return 0;
+}
+
+/* Fused QKV seq->head permute, element by element (c = 0, 1, 2 for q, k, v):
+ *   out[j][c][b][s*(N/p) + n][hh][d] = in[s][b][n][c][j*(H/p) + hh][d] */
+int oracle_qkv_seq_to_head(const void *in, void *out, int p, int B, int N, int H, int D,
+                           int elem_bytes)
+{
+    if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0 || elem_bytes <= 0)
+        return -1;
+    if (N % p != 0 || H % p != 0)
+        return -1;
+    const unsigned char *src = (const unsigned char *)in;
+    unsigned char *dst = (unsigned char *)out;
+    long Ns = N / p, Hs = H / p;
+    for (long s = 0; s < p; ++s)
+        for (long j = 0; j < p; ++j)
+            for (long c = 0; c < 3; ++c)
+                for (long b = 0; b < B; ++b)
+                    for (long n = 0; n < Ns; ++n)
+                        for (long hh = 0; hh < Hs; ++hh)
+                            for (long d = 0; d < D; ++d) {
+                                long si = ((((s * B + b) * Ns + n) * 3 + c) * H + (j * Hs + hh)) * D + d;
+                                long di = ((((j * 3 + c) * B + b) * (long)N + (s * Ns + n)) * Hs + hh) * D + d;
+                                memcpy(dst + di * elem_bytes, src + si * elem_bytes,
+                                       (size_t)elem_bytes);
+                            }
     return 0;
 }

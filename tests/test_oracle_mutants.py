@@ -35,8 +35,16 @@ MUTANTS = {
                                   "double w = exp(lse_parts[t * part_l + li] - M);"),
     "merge_lse_is_max": ("lse[li] = L;", "lse[li] = M;"),
     "merge_lse_index_o_order": ("long li = (b * H + h) * N + n;", "long li = (b * N + n) * H + h;"),
-    "permute_token_from_dest": ("(((j * B + b) * (long)N + (s * Ns + n))", "(((j * B + b) * (long)N + (j * Ns + n))"),
-    "permute_heads_from_src": ("(j * Hs + hh)) * D + d;", "(s * Hs + hh)) * D + d;"),
+    "permute_token_from_dest": ("long di = (((j * B + b) * (long)N + (s * Ns + n))",
+                                "long di = (((j * B + b) * (long)N + (j * Ns + n))"),
+    "permute_heads_from_src": ("long si = (((s * B + b) * Ns + n) * H + (j * Hs + hh))",
+                               "long si = (((s * B + b) * Ns + n) * H + (s * Hs + hh))"),
+    "h2s_token_from_dest": ("long si = (((j * B + b) * (long)N + (s * Ns + n))",
+                            "long si = (((j * B + b) * (long)N + (j * Ns + n))"),
+    "h2s_head_group_from_src": ("long di = (((s * B + b) * Ns + n) * H + (j * Hs + hh))",
+                                "long di = (((s * B + b) * Ns + n) * H + (s * Hs + hh))"),
+    "qkv_output_tensor_major": ("long di = ((((j * 3 + c) * B + b)", "long di = ((((c * p + j) * B + b)"),
+    "qkv_source_always_q": ("* 3 + c) * H + (j * Hs + hh)) * D + d;", "* 3 + 0) * H + (j * Hs + hh)) * D + d;"),
 }
 
 

@@ -295,6 +295,67 @@ def test_permute_rejects_nondivisible(api):
         api.permute(x, 4)
 
 
+def _head_to_seq_by_exchange(y, p):
+    """The page's sequence after attention, emulated with numpy: on each head shard split
+    the tokens into p ranges, send range s to rank s, and on rank s concatenate what
+    arrives along the head axis in source-rank order (MindIE SD page, Ulysses usage
+    example, the second all-to-all)."""
+    shards = [y[j] for j in range(p)]                   # each [B, N, H/p, D]
+    send = [np.split(sh, p, axis=1) for sh in shards]  # send[j][s]: [B, N/p, H/p, D]
+    return np.stack([np.concatenate([send[j][s] for j in range(p)], axis=2) for s in range(p)])
+
+
+def _random_bits(g, shape, dt):
+    if dt == np.float32:
+        return g.standard_normal(shape).astype(np.float32)
+    return g.integers(0, 2 ** 16 if dt != np.uint8 else 256, size=shape).astype(dt)
+
+
+@pytest.mark.parametrize("p,B,N,H,D,dt", [
+    (1, 1, 3, 2, 4, np.uint16), (2, 1, 8, 4, 3, np.uint16), (4, 2, 12, 8, 5, np.float32),
+    (4, 1, 16, 24, 2, np.uint16), (3, 1, 9, 6, 7, np.uint8),
+])
+def test_head_to_seq_index_map_and_round_trips(api, p, B, N, H, D, dt):
+    g = _rng(52)
+    y = _random_bits(g, (p, B, N, H // p, D), dt)
+    out = api.head_to_seq(y, p)
+    assert out.shape == (p, B, N // p, H, D)
+    ref1 = y.reshape(p, B, p, N // p, H // p, D).transpose(2, 1, 3, 0, 4, 5).reshape(out.shape)
+    assert out.tobytes() == ref1.tobytes()
+    assert out.tobytes() == _head_to_seq_by_exchange(y, p).tobytes()
+    # the two all-to-alls undo each other, in either order
+    assert api.permute(out, p).tobytes() == y.tobytes()
+    x = _random_bits(g, (p, B, N // p, H, D), dt)
+    assert api.head_to_seq(api.permute(x, p), p).tobytes() == x.tobytes()
+
+
+def test_head_to_seq_rejects_nondivisible(api):
+    y = np.zeros((4, 1, 6, 2, 2), np.uint16)  # 6 tokens not divisible by 4
+    with pytest.raises(ValueError):
+        api.head_to_seq(y, 4)
+
+
+@pytest.mark.parametrize("p,B,N,H,D,dt", [
+    (1, 1, 3, 2, 4, np.uint16), (2, 1, 8, 4, 3, np.uint16), (4, 2, 12, 8, 5, np.float32),
+    (3, 1, 9, 6, 7, np.uint8),
+])
+def test_qkv_permute_index_map(api, p, B, N, H, D, dt):
+    g = _rng(53)
+    x = _random_bits(g, (p, B, N // p, 3, H, D), dt)
+    out = api.qkv_permute(x, p)
+    assert out.shape == (p, 3, B, N, H // p, D)
+    # one exchange of the packed rows: split each shard's heads into p groups, send group
+    # j to rank j, concatenate along tokens in source order, then unpack q, k, v
+    send = [np.split(x[s], p, axis=3) for s in range(p)]   # send[s][j]: [B, N/p, 3, H/p, D]
+    recv = [np.concatenate([send[s][j] for s in range(p)], axis=1) for j in range(p)]
+    ref = np.stack([r.transpose(2, 0, 1, 3, 4) for r in recv])
+    assert out.tobytes() == ref.tobytes()
+    # equal to three separate permutes of the q, k and v tensors
+    for c in range(3):
+        per = api.permute(np.ascontiguousarray(x[:, :, :, c]), p)
+        assert out[:, c].tobytes() == per.tobytes()
+
+
 # ---------------------------------------------------------------- page numbers
 
 def test_page_byte_counts_and_cross_rank_traffic(api):
