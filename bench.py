@@ -8,12 +8,15 @@ call over the whole sequence; value = 4*N*N*H*D flops / step time, in TFLOP/s.
 
 Legs timed in the same run and reported under "legs":
   wan5b       attention at N=27280 (Wan2.2-TI2V-5B video tokens), 24 x 128
+  wan5b_cross Wan2.2 cross-attention: 27280 video queries x 512 text keys, 24 x 128
   flux_ring4  one GPU's FLUX Ring-4 share: Ulysses-4 permute of the Q shards, then
               Q[1152] x 4 KV chunks of 1152 through attn_fwd_lse (f32 partials), then the
               LSE merge; each kernel's time and rate
   wan14b_u8   one GPU's Wan2.1-14B Ulysses-8 share: N=75600, 5 heads, 8 KV chunks of 9450
               + merge
-  permute_wan14b  the Ulysses-8 permute at Wan2.1-14B 720p, [8,1,9450,40,128] -> [8,1,75600,5,128]
+  permute_wan14b  the Ulysses-8 permutes at Wan2.1-14B 720p: seq->head [8,1,9450,40,128] ->
+              [8,1,75600,5,128], its inverse head->seq, and the fused QKV seq->head
+              [8,1,9450,3,40,128] -> [8,3,1,75600,5,128]
 
 Inputs are seeded synthetic tensors (no dataset, no weights) already resident in
 HBM when a timed region starts.  Times come from HIP events recorded on the stream
@@ -58,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="wan5b,flux_ring4,wan14b_u8,permute_wan14b",
+    ap.add_argument("--legs", default="wan5b,wan5b_cross,flux_ring4,wan14b_u8,permute_wan14b",
                     help="comma list of extra legs (or 'none'); 'copy' adds a plain copy kernel "
                          "used to calibrate HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -226,6 +229,22 @@ def main():
         err("[bench] wan5b: %.3f ms, %.1f TFLOP/s" % (ms, tf))
         del q, k, v, o, lse
 
+    # ---------------------------------------------------------------- wan5b cross-attention
+    if "wan5b_cross" in legs_req:
+        wc = synthetic.WAN5B_CROSS
+        err("[bench] leg wan5b_cross: generating inputs")
+        q, k, v = (t.to(dev) for t in synthetic.workload_qkv(wc))
+        o = torch.empty((wc.B, wc.Nq, wc.H, wc.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((wc.B, wc.H, wc.Nq), dtype=torch.float32, device=dev)
+        ms = timer.time(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), reps=20, warmup=3)
+        tf = wc.flops / (ms * 1e-3) / 1e12
+        nbytes = 2 * wc.B * (2 * wc.Nq + 2 * wc.Nkv) * wc.H * wc.D + 4 * wc.B * wc.H * wc.Nq
+        legs["wan5b_cross"] = {"workload": wc.name, "attn_ms": round(ms, 4), "attn_tflops": round(tf, 2),
+                               "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                               "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        err("[bench] wan5b_cross: %s" % legs["wan5b_cross"])
+        del q, k, v, o, lse
+
     # ---------------------------------------------------------------- flux ring-4 share
     if "flux_ring4" in legs_req:
         w3 = synthetic.FLUX_RING4
@@ -302,19 +321,29 @@ def main():
         err("[bench] wan14b_u8: %s" % legs["wan14b_u8"])
         del q, k, v, parts, lparts, o, lse
 
-    # ---------------------------------------------------------------- permute at Wan-14B U8
+    # ---------------------------------------------------------------- permutes at Wan-14B U8
     if "permute_wan14b" in legs_req:
         p, Ns, H, D = 8, 9450, 40, 128
         err("[bench] leg permute_wan14b")
+        res = {}
+
+        def one(name, fn, x, out, shape):
+            ms = timer.time(lambda: fn(x, p, out=out), reps=10, warmup=2)
+            nbytes = 2 * x.numel() * x.element_size()
+            res[name] = {"shape": shape, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "bytes": nbytes, "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            err("[bench]   %s: %s" % (name, res[name]))
+
         x = torch.empty((p, 1, Ns, H, D), dtype=torch.bfloat16, device=dev).normal_()
-        out = torch.empty((p, 1, Ns * p, H // p, D), dtype=torch.bfloat16, device=dev)
-        ms = timer.time(lambda: dtl.seq_to_head_permute(x, p, out=out), reps=10, warmup=2)
-        nbytes = 2 * x.numel() * 2
-        legs["permute_wan14b"] = {"shape": "[8,1,9450,40,128]->[8,1,75600,5,128] bf16", "ms": round(ms, 4),
-                                  "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
-                                  "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        err("[bench] permute_wan14b: %s" % legs["permute_wan14b"])
-        del x, out
+        y = torch.empty((p, 1, Ns * p, H // p, D), dtype=torch.bfloat16, device=dev)
+        one("seq_to_head", dtl.seq_to_head_permute, x, y, "[8,1,9450,40,128]->[8,1,75600,5,128] bf16")
+        one("head_to_seq", dtl.head_to_seq_permute, y, x, "[8,1,75600,5,128]->[8,1,9450,40,128] bf16")
+        del x, y
+        x = torch.empty((p, 1, Ns, 3, H, D), dtype=torch.bfloat16, device=dev).normal_()
+        y = torch.empty((p, 3, 1, Ns * p, H // p, D), dtype=torch.bfloat16, device=dev)
+        one("qkv_seq_to_head", dtl.qkv_seq_to_head_permute, x, y, "[8,1,9450,3,40,128]->[8,3,1,75600,5,128] bf16")
+        del x, y
+        legs["permute_wan14b"] = res
 
     # ---------------------------------------------------------------- copy (counter calibration)
     if "copy" in legs_req:

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
   attn_fwd_lse(q, k, v, ...)            -> (o, lse)
   attn_merge_lse(o_parts, lse_parts, ...) -> (o, lse)
   seq_to_head_permute(x, p, ...)        -> out
+  head_to_seq_permute(y, p, ...)        -> out
+  qkv_seq_to_head_permute(x, p, ...)    -> out
 and two drivers that only sequence those calls:
   attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  one call per KV chunk
   ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge
@@ -29,7 +31,8 @@ LIB_PATH = os.path.join(_PKG, "libdtl.so")
 DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
 DTL_BF16, DTL_F32 = 0, 1
 
-EXPORTS = ("attn_fwd_lse", "attn_merge_lse", "seq_to_head_permute", "dtl_status_string")
+EXPORTS = ("attn_fwd_lse", "attn_merge_lse", "seq_to_head_permute", "head_to_seq_permute",
+           "qkv_seq_to_head_permute", "dtl_status_string")
 
 
 class DtlError(RuntimeError):
@@ -49,8 +52,9 @@ def _load_library():
     lib.attn_fwd_lse.restype = i
     lib.attn_merge_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_merge_lse.restype = i
-    lib.seq_to_head_permute.argtypes = [vp, vp, i, i, i, i, i, i, vp]
-    lib.seq_to_head_permute.restype = i
+    for name in ("seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute"):
+        getattr(lib, name).argtypes = [vp, vp, i, i, i, i, i, i, vp]
+        getattr(lib, name).restype = i
     lib.dtl_status_string.argtypes = [i]
     lib.dtl_status_string.restype = ctypes.c_char_p
     return lib
@@ -166,6 +170,49 @@ def seq_to_head_permute(x: torch.Tensor, p: int, out: Optional[torch.Tensor] = N
         raise ValueError("out must be [p,B,N,H/p,D]")
     _check(lib.seq_to_head_permute(x.data_ptr(), out.data_ptr(), p, B, N, H, D,
                                    x.element_size(), _stream(x, stream)))
+    return out
+
+
+def head_to_seq_permute(y: torch.Tensor, p: int, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Ulysses head->seq permute (after attention): y [p,B,N,H/p,D] (p head shards) ->
+    out [p,B,N/p,H,D] (p sequence shards).  Any 1/2/4/8-byte dtype; bit-exact."""
+    _dev(y, "y", None, 5)
+    p_, B, N, Hs, D = y.shape
+    if p_ != p:
+        raise ValueError("y.shape[0] must equal p")
+    if N % p != 0:
+        raise ValueError("p must divide the token count")
+    H = Hs * p
+    if out is None:
+        out = torch.empty((p, B, N // p, H, D), dtype=y.dtype, device=y.device)
+    _dev(out, "out", y.dtype, 5)
+    if tuple(out.shape) != (p, B, N // p, H, D):
+        raise ValueError("out must be [p,B,N/p,H,D]")
+    _check(lib.head_to_seq_permute(y.data_ptr(), out.data_ptr(), p, B, N, H, D,
+                                   y.element_size(), _stream(y, stream)))
+    return out
+
+
+def qkv_seq_to_head_permute(x: torch.Tensor, p: int, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Fused QKV seq->head permute: x [p,B,N/p,3,H,D] (p sequence shards of packed q, k,
+    v) -> out [p,3,B,N,H/p,D]; out[j, 0], out[j, 1], out[j, 2] are head group j's q, k, v.
+    Any 1/2/4/8-byte dtype; bit-exact."""
+    _dev(x, "x", None, 6)
+    p_, B, Ns, three, H, D = x.shape
+    if p_ != p or three != 3:
+        raise ValueError("x must be [p,B,N/p,3,H,D]")
+    if H % p != 0:
+        raise ValueError("p must divide the head count")
+    N = Ns * p
+    if out is None:
+        out = torch.empty((p, 3, B, N, H // p, D), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype, 6)
+    if tuple(out.shape) != (p, 3, B, N, H // p, D):
+        raise ValueError("out must be [p,3,B,N,H/p,D]")
+    _check(lib.qkv_seq_to_head_permute(x.data_ptr(), out.data_ptr(), p, B, N, H, D,
+                                       x.element_size(), _stream(x, stream)))
     return out
 
 

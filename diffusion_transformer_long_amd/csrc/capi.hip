@@ -5,6 +5,7 @@
 
 #include "dtl.h"
 #include "common.h"
+#include "runmap.h"
 
 namespace {
 
@@ -87,19 +88,46 @@ dtl_status attn_merge_lse(const void* o_parts, const float* lse_parts, void* o, 
     return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
 }
 
-dtl_status seq_to_head_permute(const void* in, void* out, int p, int B, int N, int H, int D,
-                               int elem_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+dtl_status permute_call(dtl::PermuteKind kind, const void* in, void* out, int p, int B, int N,
+                        int H, int D, int elem_bytes, hipStream_t stream) {
     if (!in || !out) return DTL_ERR_INVALID_ARG;
     if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
     if (N % p != 0 || H % p != 0) return DTL_ERR_INVALID_ARG;
     if (!aligned16(in) || !aligned16(out)) return DTL_ERR_INVALID_ARG;
     if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
         return DTL_ERR_UNSUPPORTED;
-    const long bytes = (long)B * N * H * D * elem_bytes;
+    const long elems = dtl::permute_elements(kind, B, N, H, D);
+    if (elems > (1l << 40)) return DTL_ERR_INVALID_ARG;  // keeps the byte count below exact
+    const long bytes = elems * elem_bytes;
     if (overlap(in, bytes, out, bytes)) return DTL_ERR_INVALID_ARG;
-    if ((long)B * N * H * D / 256 + 1 > kIntMax) return DTL_ERR_INVALID_ARG;
-    hipError_t e = dtl::launch_permute(in, out, p, B, N, H, D, elem_bytes, stream);
+    const int unit = dtl::permute_unit_bytes((long)(H / p) * D * elem_bytes);
+    if (bytes / unit > dtl::permute_max_units()) return DTL_ERR_INVALID_ARG;
+    hipError_t e = dtl::launch_permute(kind, in, out, p, B, N, H, D, elem_bytes, stream);
     return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+dtl_status seq_to_head_permute(const void* in, void* out, int p, int B, int N, int H, int D,
+                               int elem_bytes, hipStream_t stream) {
+    return permute_call(dtl::PermuteKind::SeqToHead, in, out, p, B, N, H, D, elem_bytes, stream);
+}
+
+dtl_status head_to_seq_permute(const void* in, void* out, int p, int B, int N, int H, int D,
+                               int elem_bytes, hipStream_t stream) {
+    return permute_call(dtl::PermuteKind::HeadToSeq, in, out, p, B, N, H, D, elem_bytes, stream);
+}
+
+dtl_status qkv_seq_to_head_permute(const void* in, void* out, int p, int B, int N, int H, int D,
+                                   int elem_bytes, hipStream_t stream) {
+    return permute_call(dtl::PermuteKind::QkvSeqToHead, in, out, p, B, N, H, D, elem_bytes,
+                        stream);
 }
 
 }  // extern "C"

@@ -37,7 +37,9 @@ int merge_max_parts();  // largest P attn_merge_lse accepts
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
                         int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,
                         hipStream_t stream);
-hipError_t launch_permute(const void* in, void* out, int p, int B, int N, int H, int D,
-                          int elem_bytes, hipStream_t stream);
+enum class PermuteKind;
+long permute_max_units();  // largest copy-unit count one permute call may move
+hipError_t launch_permute(PermuteKind kind, const void* in, void* out, int p, int B, int N,
+                          int H, int D, int elem_bytes, hipStream_t stream);
 
 }  // namespace dtl

@@ -122,6 +122,52 @@ dtl_status seq_to_head_permute(const void *in, void *out,
                                int p, int B, int N, int H, int D,
                                int elem_bytes, hipStream_t stream);
 
+/*
+ * head_to_seq_permute - the local data movement of the Ulysses all-to-all after
+ * attention (the inverse of seq_to_head_permute).
+ *
+ * Turns p head shards ("all N tokens x H/p heads": each rank's attention output) back
+ * into p sequence shards ("N/p tokens x all H heads"): token range s = [s*N/p,
+ * (s+1)*N/p), head groups concatenated in source-rank order (arganzheng.life section
+ * 4.1 figure, the O all-to-all that returns to the token split; MindIE SD "多卡并行"
+ * page, Ulysses usage example: split the attention output into p token ranges,
+ * exchange, concatenate along heads):
+ *     out[s][b][n][j*(H/p) + hh][d] = in[j][b][s*(N/p) + n][hh][d]
+ *
+ *   in   [p, B, N, H/p, D]    the p head shards; in[j] holds heads [j*H/p, (j+1)*H/p)
+ *   out  [p, B, N/p, H, D]    the p sequence shards; out[s] is what rank s receives
+ *   elem_bytes  1, 2, 4 or 8; the copy is bit-exact
+ *
+ * Errors: as seq_to_head_permute.
+ */
+dtl_status head_to_seq_permute(const void *in, void *out,
+                               int p, int B, int N, int H, int D,
+                               int elem_bytes, hipStream_t stream);
+
+/*
+ * qkv_seq_to_head_permute - one pass that performs seq_to_head_permute on Q, K and V
+ * together, the local data movement of a fused QKV all-to-all ("AIGC 分布式推理：从
+ * Wan2.2 理解 DP/TP/CP/SP/PP", CP section: per self-attention one fused QKV all-to-all
+ * and one for the output).  The input is the fused QKV projection's layout, each
+ * token's row holding its q, k and v of all heads side by side; the output gives every
+ * head group three separate BSND tensors that attn_fwd_lse takes directly (c = 0, 1, 2
+ * for q, k, v):
+ *     out[j][c][b][s*(N/p) + n][hh][d] = in[s][b][n][c][j*(H/p) + hh][d]
+ *
+ *   in   [p, B, N/p, 3, H, D]   the p sequence shards of packed q, k, v
+ *   out  [p, 3, B, N, H/p, D]   out[j][0], out[j][1], out[j][2]: rank j's q, k, v
+ *   elem_bytes  1, 2, 4 or 8; the copy is bit-exact
+ *
+ * Errors: as seq_to_head_permute.
+ *
+ * The three permutes move runs of (H/p)*D elements with copies of the largest of 16, 8,
+ * 4, 2 or 1 bytes that divides a run; a call of more than 2^31 - 256 such units (32 GiB
+ * with 16-byte units) is rejected with DTL_ERR_INVALID_ARG.
+ */
+dtl_status qkv_seq_to_head_permute(const void *in, void *out,
+                                   int p, int B, int N, int H, int D,
+                                   int elem_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code (never NULL). */
 const char *dtl_status_string(dtl_status s);
 

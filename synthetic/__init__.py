@@ -17,7 +17,9 @@ parallelism, section 1 communication table: N = 4608, d = 3072); the Wan2.2
 TI2V-5B video sequence of 27280 tokens with 24 heads of 128 ("AIGC 分布式推理：
 从 Wan2.2 理解 DP/TP/CP/SP/PP", model parameters); one Ulysses-8 share of
 Wan2.1-14B 720p (N = 75600, 40 heads of 128, 5 heads per GPU; arganzheng.life,
-section 1 table and section 4.1).
+section 1 table and section 4.1); Wan2.2's cross-attention, whose 27280 video queries
+attend to 512 text keys and values that every GPU holds whole ("AIGC 分布式推理", CP
+section; Q comes from the video tokens, K and V from the text).
 """
 from __future__ import annotations
 
@@ -53,7 +55,7 @@ class Workload:
         return self.Nkv // self.chunks
 
 
-# The five workloads.  The seed of each is fixed here once, not chosen after the fact.
+# The workloads.  The seed of each is fixed here once, not chosen after the fact.
 TINY_RING = Workload("tiny_ring_N256_H4_D64_kv4x64", 1, 256, 256, 4, 64, seed=1, chunks=4)
 FLUX = Workload("flux_1024_N4608_H24_D128", 1, 4608, 4608, 24, 128, seed=2, k_scale=3.0)
 FLUX_RING4 = Workload("flux_ring4_share_Nq1152_Nkv4608_H24_D128_kv4x1152", 1, 1152, 4608, 24, 128,
@@ -61,19 +63,22 @@ FLUX_RING4 = Workload("flux_ring4_share_Nq1152_Nkv4608_H24_D128_kv4x1152", 1, 11
 WAN5B = Workload("wan22_ti2v5b_N27280_H24_D128", 1, 27280, 27280, 24, 128, seed=4)
 WAN14B_U8 = Workload("wan21_14b_720p_u8_share_N75600_H5_D128_kv8x9450", 1, 75600, 75600, 5, 128,
                      seed=5, chunks=8)
+# Cross-attention: Q draws 27280 rows, then K and V 512 each.
+WAN5B_CROSS = Workload("wan22_ti2v5b_cross_Nq27280_Nkv512_H24_D128", 1, 27280, 512, 24, 128, seed=6)
 
-ALL = (TINY_RING, FLUX, FLUX_RING4, WAN5B, WAN14B_U8)
+ALL = (TINY_RING, FLUX, FLUX_RING4, WAN5B, WAN14B_U8, WAN5B_CROSS)
 BY_NAME = {w.name: w for w in ALL}
 
 
-def draw_f32(seed: int, B: int, N: int, H: int, D: int, k_scale: float = 1.0
-             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Q, K, V as float32 [B, N, H, D] in draw order Q, K, V; K scaled before rounding."""
+def draw_f32(seed: int, B: int, N: int, H: int, D: int, k_scale: float = 1.0,
+             n_kv: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Q as float32 [B, N, H, D], then K and V as [B, n_kv (default N), H, D], in draw
+    order Q, K, V; K scaled before rounding."""
     g = np.random.Generator(np.random.PCG64(seed))
-    shape = (B, N, H, D)
-    q = g.standard_normal(shape, dtype=np.float32)
-    k = g.standard_normal(shape, dtype=np.float32)
-    v = g.standard_normal(shape, dtype=np.float32)
+    n_kv = N if n_kv is None else n_kv
+    q = g.standard_normal((B, N, H, D), dtype=np.float32)
+    k = g.standard_normal((B, n_kv, H, D), dtype=np.float32)
+    v = g.standard_normal((B, n_kv, H, D), dtype=np.float32)
     if k_scale != 1.0:
         k *= np.float32(k_scale)
     return q, k, v
@@ -88,11 +93,9 @@ def to_bf16(x: np.ndarray):
 def workload_qkv(w: Workload):
     """bf16 CPU tensors (q, k, v) of one workload: q is [B, Nq, H, D] (its Q block),
     k and v are [B, Nkv, H, D]."""
-    n_full = max(w.Nkv, w.q_row0 + w.Nq)
-    q, k, v = draw_f32(w.seed, w.B, n_full, w.H, w.D, w.k_scale)
+    n_q = max(w.Nkv, w.q_row0 + w.Nq)   # a Q block is cut from the full sequence's draw
+    q, k, v = draw_f32(w.seed, w.B, n_q, w.H, w.D, w.k_scale, n_kv=w.Nkv)
     q = q[:, w.q_row0:w.q_row0 + w.Nq]
-    k = k[:, :w.Nkv]
-    v = v[:, :w.Nkv]
     return to_bf16(q), to_bf16(k), to_bf16(v)
 
 

@@ -1,6 +1,8 @@
 // Host-side checks of the index helpers the kernels use (built with hipcc, run on the CPU).
 //   fastdiv: FastDiv::div(n) == n / d for edge and random n, many d
 //   xcd:     xcd_contiguous is a bijection on [0, total) for many totals
+//   runmap:  for the three permutes and many shapes, RunMap::source agrees with the
+//            element index map written out directly, stays in bounds and is a bijection
 #include <stdio.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -8,6 +10,7 @@
 
 #include "common.h"
 #include "fastdiv.h"
+#include "runmap.h"
 
 static uint64_t rng = 0x9E3779B97F4A7C15ull;
 static uint32_t next32() {  // xorshift64*
@@ -39,6 +42,53 @@ int main() {
             if (l < 0 || l >= total || seen[l]++) { if (bad < 10) printf("xcd total=%d pid=%d -> %d\n", total, pid, l); ++bad; }
         }
     }
+    // element source of output element o, written out from each map's definition
+    auto direct = [](dtl::PermuteKind kind, long p, long B, long N, long H, long D, long o) -> long {
+        const long Ns = N / p, Hs = H / p;
+        long d = o % D; o /= D;
+        long hh = o % Hs; o /= Hs;
+        if (kind == dtl::PermuteKind::HeadToSeq) {   // out [s][b][n][j*Hs + hh][d]
+            long j = o % p; o /= p;
+            long n = o % Ns; o /= Ns;
+            long b = o % B; long s = o / B;
+            return (((j * B + b) * N + s * Ns + n) * Hs + hh) * D + d;
+        }
+        long tok = o % N; o /= N;
+        long b = o % B; o /= B;
+        long s = tok / Ns, n = tok % Ns;
+        if (kind == dtl::PermuteKind::SeqToHead) {   // out [j][b][tok][hh][d]
+            long j = o;
+            return (((s * B + b) * Ns + n) * H + j * Hs + hh) * D + d;
+        }
+        long c = o % 3; long j = o / 3;              // out [j][c][b][tok][hh][d]
+        return ((((s * B + b) * Ns + n) * 3 + c) * H + j * Hs + hh) * D + d;
+    };
+    const int shapes[][5] = {{1, 1, 3, 2, 4}, {2, 1, 8, 4, 3}, {4, 2, 12, 8, 5}, {4, 1, 16, 24, 2},
+                             {3, 1, 9, 6, 7}, {4, 1, 8, 24, 128}, {8, 1, 16, 40, 128}, {2, 3, 6, 2, 64},
+                             {5, 2, 10, 5, 8}, {1, 2, 7, 3, 1}, {6, 1, 12, 12, 1}, {2, 1, 4, 4, 6}};
+    const dtl::PermuteKind kinds[] = {dtl::PermuteKind::SeqToHead, dtl::PermuteKind::HeadToSeq,
+                                      dtl::PermuteKind::QkvSeqToHead};
+    const int ebs[] = {1, 2, 4, 8};
+    for (auto& sh : shapes)
+        for (auto kind : kinds)
+            for (int eb : ebs) {
+                const int p = sh[0], B = sh[1], N = sh[2], H = sh[3], D = sh[4];
+                const dtl::RunMap m = dtl::make_run_map(kind, p, B, N, H, D, eb);
+                const long u = dtl::permute_unit_bytes((long)(H / p) * D * eb);
+                const long per = u / eb;  // elements per copy unit
+                const long elems = dtl::permute_elements(kind, B, N, H, D);
+                if ((long)m.total * per != elems) { printf("runmap total\n"); ++bad; continue; }
+                std::vector<int> seen(m.total, 0);
+                for (uint32_t e = 0; e < m.total; ++e) {
+                    const long src = m.source(e);
+                    if (src < 0 || src >= (long)m.total || seen[src]++ ||
+                        src * per != direct(kind, p, B, N, H, D, (long)e * per)) {
+                        if (bad < 10) printf("runmap kind=%d p=%d B=%d N=%d H=%d D=%d eb=%d e=%u src=%ld\n",
+                                             (int)kind, p, B, N, H, D, eb, e, src);
+                        ++bad;
+                    }
+                }
+            }
     printf("%s (%ld failures)\n", bad ? "FAIL" : "OK", bad);
     return bad ? 1 : 0;
 }

@@ -1,11 +1,14 @@
-"""GPU parity of attn_merge_lse and seq_to_head_permute.
+"""GPU parity of attn_merge_lse and the three Ulysses permutes.
 
 Merge: Ring equivalence on GPU partials; the merge alone fed oracle partials (rounded
 to f32) against the oracle's merge of the same values; P = 1 identity; an empty
 (-inf) part; all parts empty; order of parts; bf16 partials.
-Permute: bit-exact against the oracle's index map for bf16/f32/1-byte/8-byte
-elements, the vector path and the element path, p = 1, and untouched memory past
-the output; errors for p not dividing N or H.
+Permutes (seq->head, head->seq, fused QKV seq->head): bit-exact against the oracle's
+index maps for bf16/f32/1-byte/8-byte elements, 16-byte and narrower copy units, p = 1,
+and untouched memory past the output; the round trip at the Wan2.1-14B Ulysses-8
+shape; errors for p not dividing N or H.  Ulysses-4 on the FLUX sequence end to end
+(fused QKV permute, attention per head group, head->seq permute) against the oracle's
+attention.
 """
 import numpy as np
 import pytest
@@ -141,3 +144,110 @@ def test_permute_rejects_bad_divisibility():
     x = torch.zeros((4, 1, 3, 8, 8), dtype=torch.bfloat16, device=DEV)
     st = dtl.lib.seq_to_head_permute(x.data_ptr(), x.data_ptr() + x.numel() * 2 + 4096, 4, 1, 14, 8, 8, 2, None)
     assert st == dtl.DTL_ERR_INVALID_ARG  # p does not divide N: rejected before any launch
+
+
+PERMUTE_SHAPES = [
+    (4, 1, 4608, 24, 128, torch.bfloat16),   # the FLUX Ulysses-4 shape
+    (2, 1, 64, 24, 128, torch.bfloat16),
+    (1, 2, 10, 3, 64, torch.bfloat16),
+    (8, 1, 80, 40, 128, torch.bfloat16),
+    (4, 2, 12, 8, 3, torch.bfloat16),        # 6-byte runs: 2-byte units
+    (3, 1, 9, 6, 5, torch.float32),          # 20-byte runs: 4-byte units
+    (4, 1, 16, 4, 16, torch.uint8),
+    (2, 1, 6, 2, 4, torch.float64),
+    (5, 1, 15, 5, 1, torch.uint8),           # 1-byte runs
+]
+
+
+def _random_tensor(seed, shape, dtype):
+    g = np.random.Generator(np.random.PCG64(seed))
+    nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    return torch.from_numpy(g.integers(0, 256, size=nbytes, dtype=np.uint8)).view(dtype).reshape(shape)
+
+
+def _canaried(shape, dtype):
+    n = int(np.prod(shape))
+    canary = torch.empty((n + 64,), dtype=dtype, device=DEV)
+    canary.view(torch.uint8).fill_(0xA5)
+    return canary, canary[:n].view(shape)
+
+
+def _bytes(t):
+    return t.cpu().contiguous().view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("p,B,N,H,D,dtype", PERMUTE_SHAPES)
+def test_head_to_seq_bit_exact(p, B, N, H, D, dtype):
+    import diffusion_transformer_long_amd as dtl
+    log("head_to_seq_permute p=%d B=%d N=%d H=%d D=%d %s" % (p, B, N, H, D, dtype))
+    y = _random_tensor(N + 3 * H, (p, B, N, H // p, D), dtype)
+    canary, out = _canaried((p, B, N // p, H, D), dtype)
+    dtl.head_to_seq_permute(y.to(DEV), p, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.head_to_seq(y.view(torch.uint8).numpy(), p)   # D*elem bytes per row
+    assert _bytes(out).tobytes() == ref.tobytes()
+    assert np.all(_bytes(canary[out.numel():]) == 0xA5)
+
+
+@pytest.mark.parametrize("p,B,N,H,D,dtype", PERMUTE_SHAPES)
+def test_qkv_permute_bit_exact(p, B, N, H, D, dtype):
+    import diffusion_transformer_long_amd as dtl
+    log("qkv_seq_to_head_permute p=%d B=%d N=%d H=%d D=%d %s" % (p, B, N, H, D, dtype))
+    x = _random_tensor(N + 5 * H, (p, B, N // p, 3, H, D), dtype)
+    canary, out = _canaried((p, 3, B, N, H // p, D), dtype)
+    dtl.qkv_seq_to_head_permute(x.to(DEV), p, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.qkv_permute(x.view(torch.uint8).numpy(), p)
+    assert _bytes(out).tobytes() == ref.tobytes()
+    assert np.all(_bytes(canary[out.numel():]) == 0xA5)
+
+
+def test_ulysses8_round_trip_wan14b_shape():
+    """seq->head then head->seq returns the input bit for bit at [8,1,9450,40,128]."""
+    import diffusion_transformer_long_amd as dtl
+    log("round trip [8,1,9450,40,128] bf16")
+    x = torch.empty((8, 1, 9450, 40, 128), dtype=torch.bfloat16, device=DEV)
+    x.view(torch.int16).random_(-32768, 32767, generator=torch.Generator(DEV).manual_seed(7))
+    y = dtl.seq_to_head_permute(x, 8)
+    back = dtl.head_to_seq_permute(y, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+    # every head group's tokens are the concatenation of the sequence shards
+    assert torch.equal(y[3, 0, 9450 * 5:9450 * 6].view(torch.int16), x[5, 0, :, 15:20].view(torch.int16))
+
+
+def test_permutes_reject_bad_divisibility():
+    import diffusion_transformer_long_amd as dtl
+    y = torch.zeros((4, 1, 6, 2, 8), dtype=torch.bfloat16, device=DEV)   # 6 tokens, p = 4
+    with pytest.raises(ValueError):
+        dtl.head_to_seq_permute(y, 4)
+    x = torch.zeros((4, 1, 3, 3, 6, 8), dtype=torch.bfloat16, device=DEV)  # 6 heads, p = 4
+    with pytest.raises(ValueError):
+        dtl.qkv_seq_to_head_permute(x, 4)
+
+
+def test_ulysses4_flux_end_to_end():
+    """One Ulysses-4 attention layer on the FLUX sequence, every GPU's share on this one:
+    pack the four sequence shards' q, k, v, exchange them with the fused QKV permute,
+    attend per head group (6 heads, all 4608 tokens), bring O back with the head->seq
+    permute, and compare with attention over the whole sequence."""
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.FLUX
+    log("ulysses-4 end to end on %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)                                    # [1,4608,24,128]
+    packed = torch.stack([q, k, v], dim=2).reshape(1, 4, w.Nq // 4, 3, w.H, w.D)
+    packed = packed.transpose(0, 1).contiguous().to(DEV)                  # [4,1,1152,3,24,128]
+    qkv = dtl.qkv_seq_to_head_permute(packed, 4)                          # [4,3,1,4608,6,128]
+    o_heads = torch.empty((4, 1, w.Nq, w.H // 4, w.D), dtype=torch.bfloat16, device=DEV)
+    lse_heads = torch.empty((4, 1, w.H // 4, w.Nq), dtype=torch.float32, device=DEV)
+    for j in range(4):
+        dtl.attn_fwd_lse(qkv[j, 0], qkv[j, 1], qkv[j, 2], o=o_heads[j], lse=lse_heads[j])
+    o_seq = dtl.head_to_seq_permute(o_heads, 4)                           # [4,1,1152,24,128]
+    torch.cuda.synchronize()
+    o = o_seq.transpose(0, 1).reshape(1, w.Nq, w.H, w.D)
+    lse = lse_heads.transpose(0, 1).reshape(1, w.H, w.Nq)                 # head group j = heads 6j..6j+5
+    rows = synthetic.sample_rows(w.seed + 400, w.B, w.H, w.Nq, 4096)
+    o_ref, l_ref = oracle.attn_rows(q, k, v, rows)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    assert_close("ulysses4 O (%d rows)" % len(rows), o.float().cpu().numpy()[b, i, h].astype(np.float64), o_ref)
+    assert_close("ulysses4 LSE (%d rows)" % len(rows), lse.cpu().numpy()[b, h, i].astype(np.float64), l_ref)

@@ -9,6 +9,8 @@
   [4,1,1152,24,128] -> [4,1,4608,6,128], bit-exact over the whole tensor.
 * Wan2.2-5B (N=27280, 24 x 128): full-sequence call, sampled rows.
 * Wan2.1-14B Ulysses-8 share (N=75600, 5 x 128, KV 8 x 9450): chunks + merge, sampled rows.
+* Wan2.2 cross-attention (27280 video queries x 512 text keys, 24 x 128): full call, sampled
+  rows, bf16 and f32 outputs.
 """
 import numpy as np
 import pytest
@@ -104,3 +106,16 @@ def test_wan21_14b_ulysses8_share_kv8_merge():
     o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
     torch.cuda.synchronize()
     _check_rows("wan14b u8", w, o, lse, q, k, v, n=1024)
+
+
+def test_wan22_cross_attention_512_text_keys():
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.WAN5B_CROSS
+    log("workload %s" % w.name)
+    q, k, v = synthetic.workload_qkv(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = dtl.attn_fwd_lse(qd, kd, vd)
+    o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_rows("cross", w, o, lse, q, k, v)
+    _check_rows("cross f32-out", w, o32, lse32, q, k, v)

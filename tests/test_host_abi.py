@@ -84,13 +84,16 @@ def test_attn_merge_lse_validation():
     assert m(D=12) == UNS and m(pd=5) == UNS and m(od=9) == UNS and m(P=257) == UNS
 
 
-def test_seq_to_head_permute_validation():
+@pytest.mark.parametrize("name", ["seq_to_head_permute", "head_to_seq_permute",
+                                  "qkv_seq_to_head_permute"])
+def test_permute_validation(name):
     import diffusion_transformer_long_amd as dtl
     lib = dtl.lib
     INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+    fn = getattr(lib, name)
 
     def pm(i=A, o=Bp, p=4, B=1, N=64, H=8, D=128, eb=2):
-        return lib.seq_to_head_permute(i, o, p, B, N, H, D, eb, None)
+        return fn(i, o, p, B, N, H, D, eb, None)
     assert pm(i=None) == INV and pm(o=None) == INV
     assert pm(N=66) == INV                      # p does not divide N
     assert pm(H=6) == INV                       # p does not divide H
@@ -98,6 +101,10 @@ def test_seq_to_head_permute_validation():
     assert pm(o=A + 1024) == INV                # overlap
     assert pm(i=A + 2) == INV                   # misaligned
     assert pm(eb=3) == UNS and pm(eb=16) == UNS
+    # more than 2^31 - 256 copy units: 1-byte runs (p = H = D = 1, 1-byte elements), 2^31 of them
+    assert pm(p=1, B=2, N=1 << 30, H=1, D=1, eb=1, o=A + (1 << 33)) == INV
+    if name == "qkv_seq_to_head_permute":
+        assert pm(o=A + 3 * 64 * 8 * 128 * 2 - 16) == INV   # overlaps the 3x larger input
 
 
 def test_binding_rejects_cpu_tensors_and_bad_shapes():
@@ -108,6 +115,10 @@ def test_binding_rejects_cpu_tensors_and_bad_shapes():
         dtl.attn_fwd_lse(x, x, x)
     with pytest.raises(ValueError):
         dtl.seq_to_head_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
+    with pytest.raises(ValueError):
+        dtl.head_to_seq_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
+    with pytest.raises(ValueError):
+        dtl.qkv_seq_to_head_permute(torch.zeros((2, 1, 4, 3, 2, 8)), 2)
 
 
 def test_host_index_helpers(tmp_path):
