@@ -11,9 +11,10 @@ Legs timed in the same run and reported under "legs":
   wan5b_cross Wan2.2 cross-attention: 27280 video queries x 512 text keys, 24 x 128
   flux_ring4  one GPU's FLUX Ring-4 share: Ulysses-4 permute of the Q shards, then
               Q[1152] x 4 KV chunks of 1152 through attn_fwd_lse (f32 partials), then the
-              LSE merge; each kernel's time and rate
+              LSE merge; each kernel's time and rate; and the same share with the rounds
+              folded in by attn_fwd_lse_accumulate (no partials, no merge)
   wan14b_u8   one GPU's Wan2.1-14B Ulysses-8 share: N=75600, 5 heads, 8 KV chunks of 9450
-              + merge
+              + merge, and accumulated
   permute_wan14b  the Ulysses-8 permutes at Wan2.1-14B 720p: seq->head [8,1,9450,40,128] ->
               [8,1,75600,5,128], its inverse head->seq, and the fused QKV seq->head
               [8,1,9450,3,40,128] -> [8,3,1,75600,5,128]
@@ -280,12 +281,23 @@ def main():
             dtl.attn_fwd_lse_kv_chunks(q, k, v, w3.chunks, parts[0], lparts[0])
             dtl.attn_merge_lse(parts[0], lparts[0], o=o, lse=lse)
         ms_step = timer.time(share_step, reps=10, warmup=2)
+        o_acc = parts[1][0]
+
+        def share_step_acc():
+            dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
+            dtl.ring_attention(q, k, v, w3.chunks, accumulate=True, o_acc=o_acc, o=o, lse=lse)
+        ms_step_acc = timer.time(share_step_acc, reps=10, warmup=2)
+        ms_acc = timer.time(lambda: dtl.attn_fwd_lse_accumulate(q, k[:, C:2 * C], v[:, C:2 * C], o_acc, lse),
+                            reps=20, warmup=3)
         perm_bytes = 2 * shards.numel() * 2
         merge_bytes = (w3.chunks * w3.Nq * w3.H * (w3.D + 1) * 4) + w3.Nq * w3.H * (w3.D * 2 + 4)
         chunk_flops = 4.0 * w3.Nq * C * w3.H * w3.D
         legs["flux_ring4"] = {
             "workload": w3.name, "step_ms": round(ms_step, 4),
             "step_tflops": round(w3.flops / (ms_step * 1e-3) / 1e12, 2),
+            "step_accumulate_ms": round(ms_step_acc, 4),
+            "step_accumulate_tflops": round(w3.flops / (ms_step_acc * 1e-3) / 1e12, 2),
+            "accumulate_chunk_ms": round(ms_acc, 4),
             "permute_ms": round(ms_perm, 4), "permute_gbs": round(perm_bytes / (ms_perm * 1e-3) / 1e9, 1),
             "permute_bytes": perm_bytes,
             "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
@@ -310,11 +322,19 @@ def main():
         ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts, lparts, o=o, lse=lse), reps=10, warmup=2)
         ms_step = timer.time(lambda: dtl.ring_attention(q, k, v, w5.chunks, o_parts=parts, lse_parts=lparts,
                                                          o=o, lse=lse), reps=2, warmup=1)
+        o_acc = parts[0]
+        ms_step_acc = timer.time(lambda: dtl.ring_attention(q, k, v, w5.chunks, accumulate=True, o_acc=o_acc,
+                                                             o=o, lse=lse), reps=2, warmup=1)
+        ms_acc = timer.time(lambda: dtl.attn_fwd_lse_accumulate(q, k[:, C:2 * C], v[:, C:2 * C], o_acc, lse),
+                            reps=4, warmup=1)
         merge_bytes = (w5.chunks * w5.Nq * w5.H * (w5.D + 1) * 4) + w5.Nq * w5.H * (w5.D * 2 + 4)
         chunk_flops = 4.0 * w5.Nq * C * w5.H * w5.D
         legs["wan14b_u8"] = {
             "workload": w5.name, "step_ms": round(ms_step, 3),
             "step_tflops": round(w5.flops / (ms_step * 1e-3) / 1e12, 2),
+            "step_accumulate_ms": round(ms_step_acc, 3),
+            "step_accumulate_tflops": round(w5.flops / (ms_step_acc * 1e-3) / 1e12, 2),
+            "accumulate_chunk_ms": round(ms_acc, 4),
             "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
             "merge_ms": round(ms_merge, 4), "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
             "merge_bytes": merge_bytes, "merge_frac_of_hbm": round(merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}

@@ -8,13 +8,15 @@ library has not been built; there is no fallback.
 
 Entry points (same names as the C ABI):
   attn_fwd_lse(q, k, v, ...)            -> (o, lse)
+  attn_fwd_lse_accumulate(q, k, v, o_prev, lse_prev, ...) -> (o, lse)
   attn_merge_lse(o_parts, lse_parts, ...) -> (o, lse)
   seq_to_head_permute(x, p, ...)        -> out
   head_to_seq_permute(y, p, ...)        -> out
   qkv_seq_to_head_permute(x, p, ...)    -> out
 and two drivers that only sequence those calls:
   attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  one call per KV chunk
-  ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge
+  ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge,
+                                                                    or rounds accumulated
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ LIB_PATH = os.path.join(_PKG, "libdtl.so")
 DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
 DTL_BF16, DTL_F32 = 0, 1
 
-EXPORTS = ("attn_fwd_lse", "attn_merge_lse", "seq_to_head_permute", "head_to_seq_permute",
+EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_accumulate", "attn_merge_lse", "seq_to_head_permute", "head_to_seq_permute",
            "qkv_seq_to_head_permute", "dtl_status_string")
 
 
@@ -50,6 +52,8 @@ def _load_library():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_lse.restype = i
+    lib.attn_fwd_lse_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_lse_accumulate.restype = i
     lib.attn_merge_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_merge_lse.restype = i
     for name in ("seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute"):
@@ -120,6 +124,43 @@ def attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Nq, Nkv, H, D, scale, _dtype_code(o.dtype), _stream(q, stream)))
+    return o, lse
+
+
+def attn_fwd_lse_accumulate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            o_prev: torch.Tensor, lse_prev: torch.Tensor,
+                            o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            softmax_scale: Optional[float] = None,
+                            o_dtype: torch.dtype = torch.float32,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One Ring round: attention of q over these k/v folded into the previous result
+    (o_prev [B,Nq,H,D] f32, lse_prev [B,H,Nq] f32; lse_prev = -inf rows hold no keys yet).
+    By default the result overwrites o_prev and lse_prev (f32); pass o_dtype=bf16 (and
+    no o) for the last round's final output."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.bfloat16, 4)
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, D) or tuple(v.shape) != (B, Nkv, H, D):
+        raise ValueError("k and v must be [B, Nkv, H, D] matching q %s" % (tuple(q.shape),))
+    _dev(o_prev, "o_prev", torch.float32, 4)
+    _dev(lse_prev, "lse_prev", torch.float32, 3)
+    if tuple(o_prev.shape) != (B, Nq, H, D) or tuple(lse_prev.shape) != (B, H, Nq):
+        raise ValueError("o_prev must be [B,Nq,H,D] and lse_prev [B,H,Nq]")
+    if o is None:
+        o = o_prev if o_dtype == torch.float32 else torch.empty((B, Nq, H, D), dtype=o_dtype,
+                                                                 device=q.device)
+    if lse is None:
+        lse = lse_prev
+    _dev(o, "o", None, 4)
+    _dev(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Nq, H, D) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must be [B,Nq,H,D] and lse [B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_lse_accumulate(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_prev.data_ptr(),
+                                       lse_prev.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                       B, Nq, Nkv, H, D, scale, _dtype_code(o.dtype),
+                                       _stream(q, stream)))
     return o, lse
 
 
@@ -245,9 +286,42 @@ def ring_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: in
                    out_dtype: torch.dtype = torch.bfloat16, softmax_scale: Optional[float] = None,
                    o_parts: Optional[torch.Tensor] = None, lse_parts: Optional[torch.Tensor] = None,
                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   accumulate: bool = False, o_acc: Optional[torch.Tensor] = None,
                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Attention over all keys computed as Ring attention's rounds on one GPU: per-chunk
-    partials, then the LSE merge."""
-    o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
-                                                softmax_scale, stream)
-    return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype, stream=stream)
+    """Attention over all keys computed as Ring attention's rounds on one GPU, over
+    contiguous KV chunks [t*C, (t+1)*C) (B must be 1).
+
+    accumulate=False: per-chunk f32 partials (o_parts, lse_parts), then the LSE merge.
+    accumulate=True: the first round writes an f32 running result (o_acc, and lse), each
+    later round folds its chunk into it with attn_fwd_lse_accumulate, and the last round
+    writes the final o in out_dtype; no partials are stored."""
+    if not accumulate:
+        o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
+                                                    softmax_scale, stream)
+        return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype,
+                              stream=stream)
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    if B != 1:
+        raise ValueError("KV chunking by views needs B == 1")
+    if Nkv % chunks != 0:
+        raise ValueError("chunks must divide Nkv")
+    C = Nkv // chunks
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if chunks == 1:
+        return attn_fwd_lse(q, k, v, o=o, lse=lse, softmax_scale=softmax_scale,
+                            o_dtype=out_dtype if o is None else o.dtype, stream=stream)
+    if o_acc is None:
+        o_acc = torch.empty((B, Nq, H, D), dtype=torch.float32, device=q.device)
+    attn_fwd_lse(q, k[:, :C], v[:, :C], o=o_acc, lse=lse, softmax_scale=softmax_scale,
+                 stream=stream)
+    for t in range(1, chunks - 1):
+        attn_fwd_lse_accumulate(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C], o_acc, lse,
+                                softmax_scale=softmax_scale, stream=stream)
+    if o is None:
+        o = o_acc if out_dtype == torch.float32 else torch.empty((B, Nq, H, D), dtype=out_dtype,
+                                                                 device=q.device)
+    t = chunks - 1
+    return attn_fwd_lse_accumulate(q, k[:, t * C:], v[:, t * C:], o_acc, lse, o=o,
+                                   softmax_scale=softmax_scale, stream=stream)

@@ -94,12 +94,15 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <int D, bool OUT_F32>
+// ACCUM: continue from a previous result (o_prev, lse_prev) over other keys instead of
+// starting afresh; o and lse may then be the very arrays o_prev and lse_prev (each
+// element is read before it is written, by the same lane), so none of them is restrict.
+template <int D, bool OUT_F32, bool ACCUM>
 __global__ __launch_bounds__(kThreads, 2)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                     const uint16_t* __restrict__ v, void* __restrict__ o,
-                     float* __restrict__ lse, int Nq, int Nkv, int H, float scale_log2,
-                     int n_qtiles, int total) {
+                     const uint16_t* __restrict__ v, void* o, float* lse,
+                     const float* o_prev, const float* lse_prev,
+                     int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int total) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::kRow];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::vRow];
@@ -341,15 +344,34 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
     const float l_tot = halves_sum(l_run);
     if (qrow < Nq) {
-        const float inv = 1.0f / l_tot;
+        const long lidx = ((long)b * H + h) * Nq + qrow;
+        const float lse_cur = (m_run + log2f(l_tot)) * 0.693147180559945309f;
+        float w_cur = 1.0f / l_tot, w_prev = 0.0f, lse_out = lse_cur;
+        if constexpr (ACCUM) {
+            // L = ln(e^lse_prev + e^lse_cur); o = e^(lse_prev - L) o_prev + e^(lse_cur - L) o_cur
+            // (the across-rounds accumulation of Ring attention).  lse_prev = -inf holds no
+            // keys: its o_prev is not read.
+            const float lp = lse_prev[lidx];
+            if (lp != -INFINITY) {
+                const float mx = fmaxf(lp, lse_cur);
+                const float ep = __expf(lp - mx), ec = __expf(lse_cur - mx);
+                const float inv = 1.0f / (ep + ec);
+                w_prev = ep * inv;
+                w_cur *= ec * inv;
+                lse_out = mx + __logf(ep + ec);
+            }
+        }
         const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                f32x4 x = {acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
-                           acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv};
                 const long off = obase + db * 32 + 8 * i4;
+                f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
+                           acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
+                if constexpr (ACCUM) {
+                    if (w_prev != 0.0f) x += w_prev * *reinterpret_cast<const f32x4*>(o_prev + off);
+                }
                 if constexpr (OUT_F32) {
                     *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
                 } else {
@@ -357,34 +379,47 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                         __builtin_convertvector(x, bf16x4);
                 }
             }
-        if (g == 0)
-            lse[((long)b * H + h) * Nq + qrow] = (m_run + log2f(l_tot)) * 0.693147180559945309f;
+        if (g == 0) lse[lidx] = lse_out;
+    }
+}
+
+template <int D, bool OUT_F32, bool ACCUM>
+void launch_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
+                const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
+                float scale_log2, int n_qtiles, int total, hipStream_t stream) {
+    attn_fwd_kernel<D, OUT_F32, ACCUM><<<dim3(total), dim3(kThreads), 0, stream>>>(
+        q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total);
+}
+
+template <int D>
+void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
+              const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
+              float scale_log2, int n_qtiles, int total, bool out_f32, hipStream_t stream) {
+    const bool accum = o_prev != nullptr;
+    if (out_f32) {
+        if (accum) launch_one<D, true, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
+        else launch_one<D, true, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
+    } else {
+        if (accum) launch_one<D, false, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
+        else launch_one<D, false, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
     }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int Nq, int Nkv, int H, int D, float scale, bool out_f32,
-                           hipStream_t stream) {
+                           const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
+                           int H, int D, float scale, bool out_f32, hipStream_t stream) {
     const int n_qtiles = (Nq + kBlockM - 1) / kBlockM;
     const int total = n_qtiles * H * B;  // the caller has checked that this fits an int
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    const dim3 grid(total), block(kThreads);
     auto qq = static_cast<const uint16_t*>(q);
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
-    if (D == 128) {
-        if (out_f32)
-            attn_fwd_kernel<128, true><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
-        else
-            attn_fwd_kernel<128, false><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
-    } else {
-        if (out_f32)
-            attn_fwd_kernel<64, true><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
-        else
-            attn_fwd_kernel<64, false><<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, Nq, Nkv, H, scale_log2, n_qtiles, total);
-    }
+    if (D == 128)
+        launch_d<128>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, out_f32, stream);
+    else
+        launch_d<64>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, out_f32, stream);
     return hipGetLastError();
 }
 

@@ -33,14 +33,23 @@ const char* dtl_status_string(dtl_status s) {
     return "DTL_ERR_UNKNOWN: unknown status";
 }
 
-dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int Nq, int Nkv, int H, int D, float softmax_scale,
-                        dtl_dtype o_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of attn_fwd_lse and attn_fwd_lse_accumulate (o_prev ==
+// nullptr for the former).
+dtl_status attn_call(const void* q, const void* k, const void* v, const float* o_prev,
+                     const float* lse_prev, void* o, float* lse, int B, int Nq, int Nkv, int H,
+                     int D, float softmax_scale, dtl_dtype o_dtype, bool accum,
+                     hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return DTL_ERR_INVALID_ARG;
+    if (accum && (!o_prev || !lse_prev)) return DTL_ERR_INVALID_ARG;
     if (B <= 0 || Nq <= 0 || Nkv <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DTL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return DTL_ERR_INVALID_ARG;
+    if (accum && (!aligned16(o_prev) || !aligned16(lse_prev))) return DTL_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return DTL_ERR_UNSUPPORTED;
     if (o_dtype != DTL_BF16 && o_dtype != DTL_F32) return DTL_ERR_UNSUPPORTED;
     const long q_bytes = (long)B * Nq * H * D * 2;
@@ -52,13 +61,43 @@ dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, fl
         overlap(lse, l_bytes, q, q_bytes) || overlap(lse, l_bytes, k, kv_bytes) ||
         overlap(lse, l_bytes, v, kv_bytes))
         return DTL_ERR_INVALID_ARG;
+    if (accum) {
+        // in place is allowed exactly (o == o_prev with an f32 o, lse == lse_prev); any
+        // other overlap of an output with the previous result is rejected
+        const long op_bytes = (long)B * Nq * H * D * 4;
+        const bool o_same = o == (const void*)o_prev && o_dtype == DTL_F32;
+        if ((!o_same && overlap(o, o_bytes, o_prev, op_bytes)) ||
+            (lse != lse_prev && overlap(lse, l_bytes, lse_prev, l_bytes)) ||
+            overlap(o, o_bytes, lse_prev, l_bytes) || overlap(lse, l_bytes, o_prev, op_bytes))
+            return DTL_ERR_INVALID_ARG;
+    }
     const long tiles = ((long)Nq + 127) / 128 * H * B;
     if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)B * Nq * H > kIntMax ||
         (long)H * D > (1l << 24))
         return DTL_ERR_INVALID_ARG;
-    hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, B, Nq, Nkv, H, D, softmax_scale,
-                                        o_dtype == DTL_F32, stream);
+    hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, accum ? o_prev : nullptr,
+                                        accum ? lse_prev : nullptr, B, Nq, Nkv, H, D,
+                                        softmax_scale, o_dtype == DTL_F32, stream);
     return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Nq, int Nkv, int H, int D, float softmax_scale,
+                        dtl_dtype o_dtype, hipStream_t stream) {
+    return attn_call(q, k, v, nullptr, nullptr, o, lse, B, Nq, Nkv, H, D, softmax_scale,
+                     o_dtype, false, stream);
+}
+
+dtl_status attn_fwd_lse_accumulate(const void* q, const void* k, const void* v,
+                                   const float* o_prev, const float* lse_prev, void* o,
+                                   float* lse, int B, int Nq, int Nkv, int H, int D,
+                                   float softmax_scale, dtl_dtype o_dtype, hipStream_t stream) {
+    return attn_call(q, k, v, o_prev, lse_prev, o, lse, B, Nq, Nkv, H, D, softmax_scale,
+                     o_dtype, true, stream);
 }
 
 dtl_status attn_merge_lse(const void* o_parts, const float* lse_parts, void* o, float* lse,

@@ -30,9 +30,10 @@ __host__ __device__ __forceinline__ int xcd_contiguous(int pid, int total) {
 }
 
 // Launchers (validated arguments only; each returns hipGetLastError()).
+// o_prev == nullptr: a fresh result; otherwise continue from (o_prev, lse_prev).
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int B, int Nq, int Nkv, int H, int D, float scale, bool out_f32,
-                           hipStream_t stream);
+                           const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
+                           int H, int D, float scale, bool out_f32, hipStream_t stream);
 int merge_max_parts();  // largest P attn_merge_lse accepts
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
                         int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,

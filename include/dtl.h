@@ -73,6 +73,40 @@ dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
                         float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_lse_accumulate - one round of Ring attention: attention over this call's
+ * keys, folded into the result of the rounds before it.
+ *
+ * With (o_cur, lse_cur) what attn_fwd_lse would return for these keys, and for every
+ * (b, i, h):
+ *     L           = ln(exp(lse_prev[b,h,i]) + exp(lse_cur))
+ *     o[b,i,h,:]  = exp(lse_prev - L) * o_prev[b,i,h,:] + exp(lse_cur - L) * o_cur
+ *     lse[b,h,i]  = L
+ * i.e. the online-softmax accumulation that each Ring round performs on its block of
+ * K/V (arganzheng.life, multi-GPU diffusion parallelism, section 4.2 "Ring"; MindIE SD
+ * "多卡并行" page, Ring Sequence Parallel section), done in the kernel's epilogue instead
+ * of through separate partials and attn_merge_lse.  When (o_prev, lse_prev) is the
+ * result over one key set and this call's keys are another, disjoint one, (o, lse) is
+ * attention over their union.  A row with lse_prev = -inf holds no keys yet: its o_prev
+ * is not read (it may hold anything) and the row gets this call's result alone.
+ *
+ *   q, k, v          as attn_fwd_lse
+ *   o_prev  f32 [B, Nq, H, D]   the result so far (normalised, as attn_fwd_lse writes it)
+ *   lse_prev f32 [B, H, Nq]
+ *   o       o_dtype [B, Nq, H, D]  f32 to continue with further rounds, bf16 after the last
+ *   lse     f32 [B, H, Nq]
+ *   o may be o_prev itself when o_dtype is DTL_F32, and lse may be lse_prev itself (in
+ *   place); any other overlap of o or lse with o_prev or lse_prev is rejected.
+ *
+ * Errors: as attn_fwd_lse, and DTL_ERR_INVALID_ARG for a null or misaligned o_prev or
+ * lse_prev or an overlap outside the in-place case.
+ */
+dtl_status attn_fwd_lse_accumulate(const void *q, const void *k, const void *v,
+                                   const float *o_prev, const float *lse_prev,
+                                   void *o, float *lse,
+                                   int B, int Nq, int Nkv, int H, int D,
+                                   float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
+
+/*
  * attn_merge_lse - exact merge of P partial attention results over disjoint key sets.
  *
  * For every (b, n, h), with parts t = 0..P-1:

@@ -69,6 +69,26 @@ def test_attn_fwd_lse_validation():
     assert _attn(lib, dt=7) == UNS
 
 
+def test_attn_fwd_lse_accumulate_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+    F = 0x60000000  # o_prev
+    G = 0x70000000  # lse_prev
+
+    def acc(q=A, k=Bp, v=C, op=F, lp=G, o=Dp, lse=E, B=1, Nq=128, Nkv=128, H=2, D=128, sc=0.088, dt=1):
+        return lib.attn_fwd_lse_accumulate(q, k, v, op, lp, o, lse, B, Nq, Nkv, H, D, sc, dt, None)
+    assert acc(op=None) == INV and acc(lp=None) == INV and acc(o=None) == INV
+    assert acc(op=F + 4) == INV and acc(lp=G + 8) == INV          # misaligned
+    assert acc(o=F + 1024) == INV                                  # overlaps o_prev, not in place
+    assert acc(o=F, dt=0) == INV                                   # bf16 output over the f32 o_prev
+    assert acc(lse=G + 16) == INV                                  # overlaps lse_prev, not in place
+    assert acc(lse=F + 64) == INV                                  # lse inside o_prev
+    assert acc(o=G) == INV                                         # o over lse_prev
+    assert acc(Nq=0) == INV and acc(sc=0.0) == INV
+    assert acc(D=96) == UNS and acc(dt=3) == UNS
+
+
 def test_attn_merge_lse_validation():
     import diffusion_transformer_long_amd as dtl
     lib = dtl.lib
