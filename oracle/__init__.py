@@ -19,6 +19,12 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
                     permute in both orders.
   qkv_permute     : the exchange emulation on a packed [.., 3, H, D] tensor, and
                     per-tensor agreement with permute on the q, k, v slices.
+  qkv_norm_rope   : closed forms (constant rows, gamma, zero angles, quarter turns),
+                    invariances (scale of x, norm of each rotated pair), RoPE's
+                    relative-position property on the 3D tables, a decimal brute force,
+                    agreement with qkv_permute on v.
+  rope_3d_angles  : positions of a (frames, rows, cols) grid, each axis owning a slice
+                    of the head's pairs; pinned through the relative-position property.
 """
 from __future__ import annotations
 
@@ -56,6 +62,8 @@ class Api:
         lib.oracle_head_to_seq.restype = i
         lib.oracle_qkv_seq_to_head.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i, i, i, i, i, i]
         lib.oracle_qkv_seq_to_head.restype = i
+        lib.oracle_qkv_norm_rope.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, ctypes.c_double]
+        lib.oracle_qkv_norm_rope.restype = i
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i
         self.lib = lib
@@ -158,6 +166,47 @@ class Api:
             raise ValueError("oracle_qkv_seq_to_head: bad sizes")
         return out
 
+    def qkv_norm_rope(self, x, gamma_q, gamma_k, cos, sin, p: int, eps: float = 1e-6) -> np.ndarray:
+        """QK-RMSNorm over each token's H*D values, rotary embedding of each head's
+        (2i, 2i+1) pairs by cos/sin[token, i], v unchanged, written in the fused QKV
+        seq->head layout: x [p,B,N/p,3,H,D] -> [p,3,B,N,H/p,D] float64."""
+        x = _f64(x)
+        P_, B, Ns, three, H, D = x.shape
+        assert P_ == p and three == 3
+        N = Ns * p
+        gq, gk = _f64(gamma_q).reshape(-1), _f64(gamma_k).reshape(-1)
+        cs, sn = _f64(cos), _f64(sin)
+        assert gq.size == H * D and gk.size == H * D
+        assert cs.shape == (N, D // 2) and sn.shape == (N, D // 2)
+        out = np.empty((p, 3, B, N, H // p, D), np.float64)
+        rc = self.lib.oracle_qkv_norm_rope(_dp(x), _dp(gq), _dp(gk), _dp(cs), _dp(sn), _dp(out),
+                                           p, B, N, H, D, float(eps))
+        if rc != 0:
+            raise ValueError("oracle_qkv_norm_rope: bad sizes")
+        return out
+
+
+def rope_3d_angles(frames: int, rows: int, cols: int, D: int, split=None,
+                   base: float = 10000.0) -> np.ndarray:
+    """Rotary angles [F*R*C, D/2] (float64) of a (frame, row, col) token grid, tokens in
+    row-major grid order (the flattening of a latent video grid into tokens).  The head's
+    D/2 rotation pairs are divided among the three axes, `split` pairs each (default: as
+    evenly as possible, the remainder to frames), and pair i of an axis that owns d_a
+    pairs turns by pos_a * base^(-i / d_a), the one-axis rotary frequencies."""
+    half = D // 2
+    if split is None:
+        hw = half // 3
+        split = (half - 2 * hw, hw, hw)
+    assert sum(split) == half
+    f, r, c = np.meshgrid(np.arange(frames), np.arange(rows), np.arange(cols), indexing="ij")
+    pos = [f.reshape(-1).astype(np.float64), r.reshape(-1).astype(np.float64),
+           c.reshape(-1).astype(np.float64)]
+    cols_out = []
+    for a, d_a in enumerate(split):
+        inv = base ** (-np.arange(d_a, dtype=np.float64) / d_a)
+        cols_out.append(np.outer(pos[a], inv))
+    return np.concatenate(cols_out, axis=1)
+
 
 def _f64(x) -> np.ndarray:
     """Accept numpy arrays or torch tensors (any float dtype); exact upcast to float64."""
@@ -223,3 +272,7 @@ def head_to_seq(x, p: int):
 
 def qkv_permute(x, p: int):
     return api().qkv_permute(x, p)
+
+
+def qkv_norm_rope(x, gamma_q, gamma_k, cos, sin, p: int, eps: float = 1e-6):
+    return api().qkv_norm_rope(x, gamma_q, gamma_k, cos, sin, p, eps)

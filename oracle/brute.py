@@ -10,6 +10,10 @@ sums at 50 significant digits.
   merge (arganzheng.life, multi-GPU diffusion parallelism, section 4.2, the
   online-softmax accumulation across Ring rounds):
       W_t = exp(lse_t);  o = sum_t W_t o_t / sum_t W_t;  lse = ln sum_t W_t.
+  QK-RMSNorm + rotary embedding of one token's hidden vector ("AIGC 分布式推理：从 Wan2.2
+  理解 DP/TP/CP/SP/PP", TP section: the norm spans all heads; RoPE acts by position):
+      y = x * gamma / sqrt(sum(x^2) / len(x) + eps); each head's pair (y_2i, y_2i+1)
+      multiplied, as a complex number y_2i + i y_2i+1, by cos_i + i sin_i.
 """
 from __future__ import annotations
 
@@ -73,3 +77,24 @@ def merge_row(o_parts: Sequence[Sequence], lse_parts: Sequence) -> Tuple[List[De
         o = [sum((W[t] * _d(o_parts[t][d]) for t in range(len(W))), Decimal(0)) / total
              for d in range(D)]
         return o, total.ln()
+
+
+def norm_rope_token(x: Sequence, gamma: Sequence, cos: Sequence, sin: Sequence, D: int,
+                    eps) -> List[Decimal]:
+    """One token's q (or k): x and gamma have H*D values, cos/sin the D/2 values of the
+    token's position.  Returns H*D decimals."""
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        xd = [_d(a) for a in x]
+        n = len(xd)
+        ms = sum((a * a for a in xd), Decimal(0)) / Decimal(n)
+        inv = Decimal(1) / (ms + _d(eps)).sqrt()
+        y = [xd[e] * inv * _d(gamma[e]) for e in range(n)]
+        out = []
+        for h in range(n // D):
+            for i in range(D // 2):
+                re, im = y[h * D + 2 * i], y[h * D + 2 * i + 1]
+                c, s_ = _d(cos[i]), _d(sin[i])
+                out.append(re * c - im * s_)
+                out.append(re * s_ + im * c)
+        return out

@@ -273,3 +273,64 @@ int oracle_qkv_seq_to_head(const void *in, void *out, int p, int B, int N, int H
                             }
     return 0;
 }
+
+/* QK-RMSNorm and rotary position embedding on packed q, k, v, written in the fused QKV
+ * seq->head layout ("AIGC 分布式推理：从 Wan2.2 理解 DP/TP/CP/SP/PP", TP section: the
+ * QK RMSNorm normalises across heads, i.e. over a token's whole H*D hidden vector, and
+ * 3D RoPE acts by token position, independent of the head split; CP section: the RoPE
+ * cos/sin are sliced with the same token range as the tokens).  For token t = s*(N/p) + n
+ * and c = 0 (q) or 1 (k), over the token's H*D values x:
+ *     r   = 1 / sqrt(mean(x^2) + eps)
+ *     y_e = x_e * r * gamma_c[e]                       e = h*D + d
+ *     per head, per pair i < D/2 (elements 2i, 2i+1 of the head):
+ *     out_2i   = y_2i cos[t][i] - y_2i+1 sin[t][i]
+ *     out_2i+1 = y_2i sin[t][i] + y_2i+1 cos[t][i]
+ * and v (c = 2) is copied unchanged.  Layouts: in [p,B,N/p,3,H,D], gamma_q/gamma_k [H*D],
+ * cos/sin [N, D/2] (the positions of the whole sequence), out [p,3,B,N,H/p,D]. */
+int oracle_qkv_norm_rope(const double *in, const double *gamma_q, const double *gamma_k,
+                         const double *cs, const double *sn, double *out,
+                         int p, int B, int N, int H, int D, double eps)
+{
+    if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0 || D % 2 != 0 || !(eps >= 0.0))
+        return -1;
+    if (N % p != 0 || H % p != 0)
+        return -1;
+    long Ns = N / p, Hs = H / p, HD = (long)H * D;
+    long ntok = (long)p * B * Ns;
+#pragma omp parallel for schedule(static)
+    for (long tk = 0; tk < ntok; ++tk) {
+        long s = tk / (B * Ns), b = (tk / Ns) % B, n = tk % Ns;
+        long t = s * Ns + n;
+        double *y = (double *)malloc(sizeof(double) * HD);
+        for (long c = 0; c < 3; ++c) {
+            const double *x = in + (((s * B + b) * Ns + n) * 3 + c) * HD;
+            if (c < 2) {
+                const double *gam = c == 0 ? gamma_q : gamma_k;
+                double ss = 0.0;
+                for (long e = 0; e < HD; ++e)
+                    ss += x[e] * x[e];
+                double r = 1.0 / sqrt(ss / (double)HD + eps);
+                for (long e = 0; e < HD; ++e)
+                    y[e] = x[e] * r * gam[e];
+                for (long h = 0; h < H; ++h)
+                    for (long i = 0; i < D / 2; ++i) {
+                        double a = y[h * D + 2 * i], bb = y[h * D + 2 * i + 1];
+                        double co = cs[t * (D / 2) + i], si = sn[t * (D / 2) + i];
+                        y[h * D + 2 * i] = a * co - bb * si;
+                        y[h * D + 2 * i + 1] = a * si + bb * co;
+                    }
+            } else {
+                for (long e = 0; e < HD; ++e)
+                    y[e] = x[e];
+            }
+            for (long h = 0; h < H; ++h) {
+                long j = h / Hs, hh = h % Hs;
+                double *dst = out + ((((j * 3 + c) * B + b) * (long)N + t) * Hs + hh) * D;
+                for (long d = 0; d < D; ++d)
+                    dst[d] = y[h * D + d];
+            }
+        }
+        free(y);
+    }
+    return 0;
+}

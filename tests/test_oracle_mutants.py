@@ -44,6 +44,15 @@ MUTANTS = {
     "h2s_head_group_from_src": ("long di = (((s * B + b) * Ns + n) * H + (j * Hs + hh))",
                                 "long di = (((s * B + b) * Ns + n) * H + (s * Hs + hh))"),
     "qkv_output_tensor_major": ("long di = ((((j * 3 + c) * B + b)", "long di = ((((c * p + j) * B + b)"),
+    "nr_norm_over_one_head": ("for (long e = 0; e < HD; ++e)\n                    ss += x[e] * x[e];",
+                              "for (long e = 0; e < D; ++e)\n                    ss += x[e] * x[e];"),
+    "nr_eps_outside_sqrt": ("1.0 / sqrt(ss / (double)HD + eps);", "1.0 / (sqrt(ss / (double)HD) + eps);"),
+    "nr_gamma_k_for_q": ("c == 0 ? gamma_q : gamma_k;", "c == 0 ? gamma_k : gamma_k;"),
+    "nr_sin_sign": ("y[h * D + 2 * i] = a * co - bb * si;", "y[h * D + 2 * i] = a * co + bb * si;"),
+    "nr_position_within_shard": ("long t = s * Ns + n;\n        double *y", "long t = n;\n        double *y"),
+    "nr_half_split_pairs": ("double a = y[h * D + 2 * i], bb = y[h * D + 2 * i + 1];",
+                            "double a = y[h * D + i], bb = y[h * D + i + D / 2];"),
+    "nr_rope_on_v": ("if (c < 2) {", "if (c < 3) {"),
     "qkv_source_always_q": ("* 3 + c) * H + (j * Hs + hh)) * D + d;", "* 3 + 0) * H + (j * Hs + hh)) * D + d;"),
 }
 

@@ -386,3 +386,116 @@ def test_page_byte_counts_and_cross_rank_traffic(api):
         x = np.zeros((p, 1, N // p, H, 1), np.uint8)
         assert list(x.shape[2:4]) == own["before"]
         assert list(api.permute(x, p).shape[2:4]) == own["after"]
+
+
+# ---------------------------------------------------------------- QK-RMSNorm + RoPE
+
+def _nr_inputs(g, p, B, N, H, D):
+    x = g.standard_normal((p, B, N // p, 3, H, D))
+    gq = 0.5 + g.random(H * D)
+    gk = 0.5 + g.random(H * D)
+    ang = g.uniform(-4, 4, size=(N, D // 2))
+    return x, gq, gk, np.cos(ang), np.sin(ang)
+
+
+@pytest.mark.parametrize("p,B,N,H,D,eps", [(1, 1, 3, 2, 4, 1e-6), (2, 2, 4, 4, 6, 0.5), (3, 1, 6, 3, 2, 0.0)])
+def test_norm_rope_matches_decimal_brute_force(api, p, B, N, H, D, eps):
+    g = _rng(61)
+    x, gq, gk, cs, sn = _nr_inputs(g, p, B, N, H, D)
+    out = api.qkv_norm_rope(x, gq, gk, cs, sn, p, eps)
+    Ns, Hs = N // p, H // p
+    worst = 0.0
+    for s in range(p):
+        for b in range(B):
+            for n in range(Ns):
+                t = s * Ns + n
+                for c, gam in ((0, gq), (1, gk)):
+                    ref = brute.norm_rope_token(x[s, b, n, c].reshape(-1), gam, cs[t], sn[t], D, eps)
+                    for h in range(H):
+                        for d in range(D):
+                            got = out[h // Hs, c, b, t, h % Hs, d]
+                            worst = max(worst, abs(float(ref[h * D + d]) - got))
+                for h in range(H):   # v: copied unchanged
+                    assert np.array_equal(out[h // Hs, 2, b, t, h % Hs], x[s, b, n, 2, h])
+    assert worst <= 1e-12, worst
+
+
+def test_norm_rope_closed_forms(api):
+    g = _rng(62)
+    p, B, N, H, D = 2, 1, 4, 2, 8
+    zero = np.zeros((N, D // 2))
+    one = np.ones((N, D // 2))
+    ones = np.ones(H * D)
+    # a constant row a: y = sign(a) / sqrt(1 + eps / a^2); with gamma the factor applies per element
+    x = np.full((p, B, N // p, 3, H, D), -2.0)
+    out = api.qkv_norm_rope(x, ones, 3 * ones, one, zero, p, eps=0.0)
+    assert np.allclose(out[:, 0], -1.0, rtol=0, atol=1e-15) and np.allclose(out[:, 1], -3.0, atol=1e-15)
+    out = api.qkv_norm_rope(x, ones, ones, one, zero, p, eps=4.0)
+    assert np.allclose(out[:, 0], -1.0 / np.sqrt(2.0), atol=1e-15)
+    # zero angles, eps = 0: scale invariance, and every token's q has mean square gamma^2 = 1
+    x = g.standard_normal((p, B, N // p, 3, H, D))
+    a = api.qkv_norm_rope(x, ones, ones, one, zero, p, eps=0.0)
+    b_ = api.qkv_norm_rope(7.5 * x, ones, ones, one, zero, p, eps=0.0)
+    assert np.allclose(a[:, :2], b_[:, :2], atol=1e-13)
+    tok = a[:, 0, 0].transpose(1, 0, 2, 3).reshape(N, H * D)      # [N, H*D] per token
+    assert np.allclose(np.mean(tok ** 2, axis=1), 1.0, atol=1e-13)
+    # quarter turn on every pair: (y_2i, y_2i+1) -> (-y_2i+1, y_2i)
+    q = api.qkv_norm_rope(x, ones, ones, zero, one, p, eps=0.0)
+    assert np.allclose(q[:, :2, ..., 0::2], -a[:, :2, ..., 1::2], atol=1e-14)
+    assert np.allclose(q[:, :2, ..., 1::2], a[:, :2, ..., 0::2], atol=1e-14)
+    # random angles keep each pair's length
+    ang = g.uniform(-3, 3, size=(N, D // 2))
+    r = api.qkv_norm_rope(x, ones, ones, np.cos(ang), np.sin(ang), p, eps=0.0)
+    assert np.allclose(r[..., 0::2] ** 2 + r[..., 1::2] ** 2, a[..., 0::2] ** 2 + a[..., 1::2] ** 2, atol=1e-12)
+    # the head mixing of the norm: doubling head 0 changes head 1's output
+    x2 = x.copy()
+    x2[..., 0, :] *= 2.0
+    c = api.qkv_norm_rope(x2, ones, ones, one, zero, p, eps=0.0)
+    assert not np.allclose(c[1, :2], a[1, :2])       # head 1 (head group 1 at p = H = 2)
+    # v is the fused QKV permute's v
+    assert r[:, 2].tobytes() == api.qkv_permute(x, p)[:, 2].tobytes()
+
+
+def test_rope_3d_angles_structure(api):
+    F, R, C, D = 3, 4, 5, 128
+    A = oracle.rope_3d_angles(F, R, C, D)
+    assert A.shape == (F * R * C, D // 2)
+    idx = lambda f, r, c: (f * R + r) * C + c
+    assert np.all(A[idx(0, 0, 0)] == 0)
+    ef, er, ec = A[idx(1, 0, 0)], A[idx(0, 1, 0)], A[idx(0, 0, 1)]
+    dt, dh = 22, 21   # the default division of 64 pairs: 22 frames, 21 rows, 21 cols
+    assert np.all(ef[dt:] == 0) and np.all(er[:dt] == 0) and np.all(er[dt + dh:] == 0)
+    assert np.all(ec[:dt + dh] == 0)
+    for part in (ef[:dt], er[dt:dt + dh], ec[dt + dh:]):
+        # pair 0 turns by the position itself; each next pair base^(-1/d) slower
+        assert part[0] == 1.0
+        ratio = part[1:] / part[:-1]
+        assert np.allclose(ratio, 10000.0 ** (-1.0 / len(part)), rtol=1e-13)
+        assert part[-1] > 1e-4
+    for f in range(F):           # angles are linear in each position
+        for r in range(R):
+            for c in range(C):
+                assert np.allclose(A[idx(f, r, c)], f * ef + r * er + c * ec, rtol=0, atol=1e-12)
+
+
+def test_rope_relative_position_property(api):
+    """q.k after the embedding depends only on the position difference of the two
+    tokens (the property rotary embeddings are built for), on the 3D grid tables."""
+    g = _rng(63)
+    F, R, C, H, D = 2, 3, 4, 1, 12
+    N = F * R * C
+    A = oracle.rope_3d_angles(F, R, C, D)
+    qv = g.standard_normal(H * D)
+    kv = g.standard_normal(H * D)
+    x = np.zeros((1, 1, N, 3, H, D))
+    x[0, 0, :, 0] = qv.reshape(H, D)
+    x[0, 0, :, 1] = kv.reshape(H, D)
+    ones = np.ones(H * D)
+    out = api.qkv_norm_rope(x, ones, ones, np.cos(A), np.sin(A), 1, eps=0.0)
+    qo, ko = out[0, 0, 0, :, 0], out[0, 1, 0, :, 0]   # [N, D]
+    idx = lambda f, r, c: (f * R + r) * C + c
+    d1 = qo[idx(1, 2, 3)] @ ko[idx(0, 1, 1)]
+    d2 = qo[idx(1, 1, 2)] @ ko[idx(0, 0, 0)]          # the same difference (1, 1, 2)
+    d3 = qo[idx(1, 1, 3)] @ ko[idx(0, 0, 0)]          # another difference
+    assert abs(d1 - d2) <= 1e-12 * max(1.0, abs(d1))
+    assert abs(d1 - d3) > 1e-3
