@@ -17,7 +17,8 @@ Legs timed in the same run and reported under "legs":
               + merge, and accumulated
   permute_wan14b  the Ulysses-8 permutes at Wan2.1-14B 720p: seq->head [8,1,9450,40,128] ->
               [8,1,75600,5,128], its inverse head->seq, and the fused QKV seq->head
-              [8,1,9450,3,40,128] -> [8,3,1,75600,5,128]
+              [8,1,9450,3,40,128] -> [8,3,1,75600,5,128], and that pass with QK-RMSNorm +
+              RoPE fused in (qkv_norm_rope_permute)
 
 Inputs are seeded synthetic tensors (no dataset, no weights) already resident in
 HBM when a timed region starts.  Times come from HIP events recorded on the stream
@@ -362,7 +363,15 @@ def main():
         x = torch.empty((p, 1, Ns, 3, H, D), dtype=torch.bfloat16, device=dev).normal_()
         y = torch.empty((p, 3, 1, Ns * p, H // p, D), dtype=torch.bfloat16, device=dev)
         one("qkv_seq_to_head", dtl.qkv_seq_to_head_permute, x, y, "[8,1,9450,3,40,128]->[8,3,1,75600,5,128] bf16")
-        del x, y
+        # the same pass with QK-RMSNorm and rotary embedding fused in (tables: seeded angles)
+        g = torch.Generator(device="cpu").manual_seed(9)
+        gq = (0.5 + torch.rand(H * D, generator=g)).to(dev)
+        gk = (0.5 + torch.rand(H * D, generator=g)).to(dev)
+        ang = (torch.rand((Ns * p, D // 2), generator=g) * 12.0 - 6.0).to(dev)
+        cs, sn = torch.cos(ang), torch.sin(ang)
+        one("qkv_norm_rope", lambda a, p_, out: dtl.qkv_norm_rope_permute(a, gq, gk, cs, sn, p_, out=out),
+            x, y, "[8,1,9450,3,40,128]->[8,3,1,75600,5,128] bf16, QK-RMSNorm + RoPE fused")
+        del x, y, gq, gk, ang, cs, sn
         legs["permute_wan14b"] = res
 
     # ---------------------------------------------------------------- copy (counter calibration)

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   seq_to_head_permute(x, p, ...)        -> out
   head_to_seq_permute(y, p, ...)        -> out
   qkv_seq_to_head_permute(x, p, ...)    -> out
+  qkv_norm_rope_permute(x, gamma_q, gamma_k, cos, sin, p, ...) -> out
 and two drivers that only sequence those calls:
   attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  one call per KV chunk
   ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge,
@@ -34,7 +35,7 @@ DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
 DTL_BF16, DTL_F32 = 0, 1
 
 EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_accumulate", "attn_merge_lse", "seq_to_head_permute", "head_to_seq_permute",
-           "qkv_seq_to_head_permute", "dtl_status_string")
+           "qkv_seq_to_head_permute", "qkv_norm_rope_permute", "dtl_status_string")
 
 
 class DtlError(RuntimeError):
@@ -59,6 +60,8 @@ def _load_library():
     for name in ("seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute"):
         getattr(lib, name).argtypes = [vp, vp, i, i, i, i, i, i, vp]
         getattr(lib, name).restype = i
+    lib.qkv_norm_rope_permute.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.qkv_norm_rope_permute.restype = i
     lib.dtl_status_string.argtypes = [i]
     lib.dtl_status_string.restype = ctypes.c_char_p
     return lib
@@ -254,6 +257,39 @@ def qkv_seq_to_head_permute(x: torch.Tensor, p: int, out: Optional[torch.Tensor]
         raise ValueError("out must be [p,3,B,N,H/p,D]")
     _check(lib.qkv_seq_to_head_permute(x.data_ptr(), out.data_ptr(), p, B, N, H, D,
                                        x.element_size(), _stream(x, stream)))
+    return out
+
+
+def qkv_norm_rope_permute(x: torch.Tensor, gamma_q: torch.Tensor, gamma_k: torch.Tensor,
+                          cos: torch.Tensor, sin: torch.Tensor, p: int, eps: float = 1e-6,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """QK-RMSNorm (over each token's H*D values) and rotary embedding of each head's
+    (2i, 2i+1) pairs by cos/sin[token, i], fused with the fused-QKV seq->head permute:
+    x bf16 [p,B,N/p,3,H,D] -> out bf16 [p,3,B,N,H/p,D]; gamma_q/gamma_k f32 [H*D];
+    cos/sin f32 [N, D/2] over the whole sequence's positions."""
+    _dev(x, "x", torch.bfloat16, 6)
+    p_, B, Ns, three, H, D = x.shape
+    if p_ != p or three != 3:
+        raise ValueError("x must be [p,B,N/p,3,H,D]")
+    if H % p != 0:
+        raise ValueError("p must divide the head count")
+    N = Ns * p
+    for t, n in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k")):
+        _dev(t, n, torch.float32, None)
+        if t.numel() != H * D:
+            raise ValueError("%s must hold H*D = %d values" % (n, H * D))
+    for t, n in ((cos, "cos"), (sin, "sin")):
+        _dev(t, n, torch.float32, 2)
+        if tuple(t.shape) != (N, D // 2):
+            raise ValueError("%s must be [N, D/2] = %s" % (n, (N, D // 2)))
+    if out is None:
+        out = torch.empty((p, 3, B, N, H // p, D), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, 6)
+    if tuple(out.shape) != (p, 3, B, N, H // p, D):
+        raise ValueError("out must be [p,3,B,N,H/p,D]")
+    _check(lib.qkv_norm_rope_permute(x.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                                     cos.data_ptr(), sin.data_ptr(), out.data_ptr(), p, B, N, H, D,
+                                     float(eps), _stream(x, stream)))
     return out
 
 

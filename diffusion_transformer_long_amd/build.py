@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdtl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["capi.hip", "attn_fwd.hip", "merge.hip", "permute.hip"]
+SOURCES = ["capi.hip", "attn_fwd.hip", "merge.hip", "permute.hip", "norm_rope.hip"]
 
 # Packed-f32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

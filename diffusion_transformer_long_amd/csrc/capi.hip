@@ -169,4 +169,29 @@ dtl_status qkv_seq_to_head_permute(const void* in, void* out, int p, int B, int 
                         stream);
 }
 
+dtl_status qkv_norm_rope_permute(const void* qkv, const float* gamma_q, const float* gamma_k,
+                                 const float* cos_t, const float* sin_t, void* out, int p, int B,
+                                 int N, int H, int D, float eps, hipStream_t stream) {
+    if (!qkv || !gamma_q || !gamma_k || !cos_t || !sin_t || !out) return DTL_ERR_INVALID_ARG;
+    if (p <= 0 || B <= 0 || N <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
+    if (N % p != 0 || H % p != 0) return DTL_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return DTL_ERR_INVALID_ARG;
+    if (!aligned16(qkv) || !aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(cos_t) ||
+        !aligned16(sin_t) || !aligned16(out))
+        return DTL_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return DTL_ERR_UNSUPPORTED;
+    if ((long)H * D > dtl::norm_rope_max_hidden()) return DTL_ERR_UNSUPPORTED;
+    if ((long)B * N * 3 > kIntMax / 2) return DTL_ERR_INVALID_ARG;
+    const long bytes = (long)B * N * 3 * H * D * 2;
+    const long g_bytes = (long)H * D * 4;
+    const long t_bytes = (long)N * (D / 2) * 4;
+    if (overlap(out, bytes, qkv, bytes) || overlap(out, bytes, gamma_q, g_bytes) ||
+        overlap(out, bytes, gamma_k, g_bytes) || overlap(out, bytes, cos_t, t_bytes) ||
+        overlap(out, bytes, sin_t, t_bytes))
+        return DTL_ERR_INVALID_ARG;
+    hipError_t e = dtl::launch_qkv_norm_rope(qkv, gamma_q, gamma_k, cos_t, sin_t, out, p, B, N, H,
+                                             D, eps, stream);
+    return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
+}
+
 }  // extern "C"

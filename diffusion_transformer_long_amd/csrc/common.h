@@ -38,6 +38,10 @@ int merge_max_parts();  // largest P attn_merge_lse accepts
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
                         int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,
                         hipStream_t stream);
+int norm_rope_max_hidden();  // largest H*D qkv_norm_rope_permute accepts
+hipError_t launch_qkv_norm_rope(const void* qkv, const float* gamma_q, const float* gamma_k,
+                                const float* cs, const float* sn, void* out, int p, int B,
+                                int N, int H, int D, float eps, hipStream_t stream);
 enum class PermuteKind;
 long permute_max_units();  // largest copy-unit count one permute call may move
 hipError_t launch_permute(PermuteKind kind, const void* in, void* out, int p, int B, int N,

@@ -202,6 +202,39 @@ dtl_status qkv_seq_to_head_permute(const void *in, void *out,
                                    int p, int B, int N, int H, int D,
                                    int elem_bytes, hipStream_t stream);
 
+/*
+ * qkv_norm_rope_permute - QK-RMSNorm and rotary position embedding of packed q, k, v,
+ * written straight into the head shards of the fused QKV all-to-all (one pass).
+ *
+ * For every token t = s*(N/p) + n (source shard s, row n; t is the position in the
+ * whole sequence) and c = 0 (q) or 1 (k), over the token's H*D hidden values x:
+ *     y_e = x_e * gamma_c[e] / sqrt(mean_e(x_e^2) + eps)          e = h*D + d
+ * then, per head h and pair i < D/2 (elements d = 2i, 2i+1 of the head):
+ *     out_2i   = y_2i * cos[t][i] - y_2i+1 * sin[t][i]
+ *     out_2i+1 = y_2i * sin[t][i] + y_2i+1 * cos[t][i]
+ * and v (c = 2) unchanged, each placed where qkv_seq_to_head_permute puts it.  The QK
+ * RMSNorm spans all heads of a token and the 3D RoPE acts by token position with cos/sin
+ * sliced by the same token range ("AIGC 分布式推理：从 Wan2.2 理解 DP/TP/CP/SP/PP", TP
+ * section and CP section); the pairing (2i, 2i+1) and the table form are this library's
+ * reading, which any multi-axis RoPE fits by its cos/sin tables.  p = 1 gives the norm and
+ * the rotation alone, out [1, 3, B, N, H, D].
+ *
+ *   qkv      bf16 [p, B, N/p, 3, H, D]   sequence shards of packed q, k, v
+ *   gamma_q  f32 [H*D], gamma_k f32 [H*D] the norms' weights
+ *   cos, sin f32 [N, D/2]               per token position of the whole sequence
+ *   out      bf16 [p, 3, B, N, H/p, D]   out[j][0..2]: head group j's q, k, v
+ *   eps      finite and >= 0
+ * Arithmetic in f32, one rounding to bf16 (nearest even) per output element.
+ *
+ * Errors: DTL_ERR_INVALID_ARG for null pointers, sizes <= 0, p not dividing N or H, a
+ * negative or non-finite eps, misalignment, or out overlapping an input;
+ * DTL_ERR_UNSUPPORTED for D not in {64, 128} or H*D > 8192.
+ */
+dtl_status qkv_norm_rope_permute(const void *qkv, const float *gamma_q, const float *gamma_k,
+                                 const float *cos, const float *sin, void *out,
+                                 int p, int B, int N, int H, int D, float eps,
+                                 hipStream_t stream);
+
 /* A static, human-readable name of a status code (never NULL). */
 const char *dtl_status_string(dtl_status s);
 

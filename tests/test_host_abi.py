@@ -89,6 +89,24 @@ def test_attn_fwd_lse_accumulate_validation():
     assert acc(D=96) == UNS and acc(dt=3) == UNS
 
 
+def test_qkv_norm_rope_permute_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+    G1, G2, CS, SN = 0x60000000, 0x61000000, 0x62000000, 0x63000000
+
+    def nr(x=A, gq=G1, gk=G2, cs=CS, sn=SN, o=Bp, p=4, B=1, N=64, H=8, D=128, eps=1e-6):
+        return lib.qkv_norm_rope_permute(x, gq, gk, cs, sn, o, p, B, N, H, D, eps, None)
+    for kw in ({"x": None}, {"gq": None}, {"gk": None}, {"cs": None}, {"sn": None}, {"o": None}):
+        assert nr(**kw) == INV, kw
+    assert nr(N=66) == INV and nr(H=6) == INV and nr(p=0) == INV
+    assert nr(eps=-1.0) == INV and nr(eps=float("inf")) == INV and nr(eps=float("nan")) == INV
+    assert nr(gq=G1 + 4) == INV and nr(o=Bp + 2) == INV
+    assert nr(o=A + 1024) == INV                 # out overlaps qkv
+    assert nr(o=CS - 1024) == INV                # out runs into the cos table
+    assert nr(D=96) == UNS and nr(H=72, p=8) == UNS   # H*D = 9216 > 8192
+
+
 def test_attn_merge_lse_validation():
     import diffusion_transformer_long_amd as dtl
     lib = dtl.lib
@@ -139,6 +157,9 @@ def test_binding_rejects_cpu_tensors_and_bad_shapes():
         dtl.head_to_seq_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
     with pytest.raises(ValueError):
         dtl.qkv_seq_to_head_permute(torch.zeros((2, 1, 4, 3, 2, 8)), 2)
+    with pytest.raises(ValueError):
+        z = torch.zeros(16)
+        dtl.qkv_norm_rope_permute(torch.zeros((2, 1, 4, 3, 2, 8), dtype=torch.bfloat16), z, z, z, z, 2)
 
 
 def test_host_index_helpers(tmp_path):
