@@ -44,9 +44,13 @@
 //
 // Full key tiles load without bounds checks from a uniform tile base plus per-thread
 // offsets fixed for the whole loop; only the ragged last tile is predicated and masked.
+#include <atomic>
+#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
+#include "streamk.h"
 
 namespace dtl {
 namespace {
@@ -65,6 +69,9 @@ constexpr int kBlockN = 64;            // keys per iteration
 #define DTL_RESCALE_THRESHOLD 2.0f
 #endif
 constexpr float kRescaleThreshold = DTL_RESCALE_THRESHOLD;
+// A tile's finaliser polls its helpers' flags at most this often (s_sleep 8 between
+// polls, ~0.2 us; the bound is ~4 ms), then computes the missing keys itself.
+constexpr int kMaxPolls = 20000;
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -94,18 +101,38 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// System-scope (write-through, uncached) 16-byte accesses for the stream-K workspace: a
+// completed store is in memory, where a workgroup on any XCD reads it, so no cache
+// maintenance is needed.  The loads are not tracked by the compiler's wait counters: the
+// caller waits (vmcnt(0)) before using the results.
+// OFF is an immediate byte offset (< 4096) from p.
+template <int OFF>
+__device__ __forceinline__ void store_sys(float* p, f32x4 x) {
+    asm volatile("global_store_dwordx4 %0, %1, off offset:%2 sc0 sc1" : : "v"(p), "v"(x), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ f32x4 load_sys(const float* p) {
+    f32x4 x;
+    asm volatile("global_load_dwordx4 %0, %1, off offset:%2 sc0 sc1" : "=v"(x) : "v"(p), "i"(OFF) : "memory");
+    return x;
+}
+
 // ACCUM: continue from a previous result (o_prev, lse_prev) over other keys instead of
 // starting afresh; o and lse may then be the very arrays o_prev and lse_prev (each
 // element is read before it is written, by the same lane), so none of them is restrict.
-template <int D, bool OUT_F32, bool ACCUM>
+// SPLIT = false: one whole tile per workgroup, tiles [tile_base, tile_base + grid).
+// SPLIT = true: the split part, tiles from tile_base on, as stream-K unit ranges.
+template <int D, bool OUT_F32, bool ACCUM, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, void* o, float* lse,
                      const float* o_prev, const float* lse_prev,
-                     int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int total) {
+                     int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int tile_base,
+                     StreamK work) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::kRow];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::vRow];
+    __shared__ int s_ready;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -113,30 +140,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int g = lane >> 5;   // lane half
     const int r = lane & 31;
 
-    const int logical = xcd_contiguous(blockIdx.x, total);
-    const int qt = logical % n_qtiles;
-    const int bh = logical / n_qtiles;
-    const int h = bh % H;
-    const int b = bh / H;
-
     const int tok_stride = H * D;  // elements between consecutive tokens (H*D <= 2^24, checked on the host)
-    const uint16_t* kbase = k + ((long)b * Nkv * H + h) * D;
-    const uint16_t* vbase = v + ((long)b * Nkv * H + h) * D;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    // Q^T fragments, held for the whole key loop.
-    const int qrow = qt * kBlockM + wave * 32 + r;
-    bf16x8 qf[D / 16];
-    {
-        const uint16_t* qp = q + (((long)b * Nq + qrow) * H + h) * D + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : zero4;
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-
-    // Per-thread tile geometry, fixed for the whole loop.
+    // Per-thread tile geometry, fixed for the whole kernel.
     //   K: chunk c covers key row k_row[c] and 8 columns; it lands in LDS row krow_slot(k_row[c]).
     //   V: a block of 4 keys (vk0..vk0+3) x 8 columns (vd0..vd0+7), stored transposed.
     int k_goff[T::kChunks], k_soff[T::kChunks], k_row[T::kChunks];
@@ -155,8 +162,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int v_soff = vd0 * T::vRow + vk0;
     static_assert(T::vPerThread == 1, "one V block per thread");
 
+    // the current tile's coordinates and state
+    const uint16_t* kbase = k;
+    const uint16_t* vbase = v;
+    int b = 0, h = 0, qrow = 0;
+    bf16x8 qf[D / 16];
     u32x4 kreg[T::kChunks];
     u32x4 vreg[4];
+    f32x16 acc[D / 32];
+    float m_run;   // reference max of this lane's query row (log2 units)
+    float l_run;   // this lane's half of the row sum, relative to m_run
 
     // Global -> registers for the tile starting at key kv0.  A full tile needs no checks;
     // the ragged last tile reads zeros past Nkv (its logits are masked below).
@@ -202,14 +217,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             }
         }
     };
-
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-    float m_run = -INFINITY;  // reference max of this lane's query row (log2 units)
-    float l_run = 0.f;        // this lane's half of the row sum, relative to m_run
 
     // Online-softmax update for one 32-key half of a tile: moves the reference max when the
     // half raises it by more than kRescaleThreshold, then rounds exp2(s*c - m) to bf16 for the
@@ -328,81 +335,249 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     using NOMASK = std::integral_constant<bool, false>;
     using MASKED = std::integral_constant<bool, true>;
 
-    const int n_full = Nkv / kBlockN;          // tiles without a ragged tail
-    const bool has_tail = Nkv % kBlockN != 0;  // one ragged tile after them
-    if (n_full > 0) load_full(0); else load_partial(0);
-    store_tile(0);
-    __syncthreads();
-    int it = 0;
-    for (; it + 1 < n_full; ++it) step(PF1{}, NOMASK{}, it);
-    if (n_full > 0) {
-        if (has_tail) step(PF2{}, NOMASK{}, it);
-        else step(PF0{}, NOMASK{}, it);
-        ++it;
-    }
-    if (has_tail) step(PF0{}, MASKED{}, it);
-
-    const float l_tot = halves_sum(l_run);
-    if (qrow < Nq) {
-        const long lidx = ((long)b * H + h) * Nq + qrow;
-        const float lse_cur = (m_run + log2f(l_tot)) * 0.693147180559945309f;
-        float w_cur = 1.0f / l_tot, w_prev = 0.0f, lse_out = lse_cur;
-        if constexpr (ACCUM) {
-            // L = ln(e^lse_prev + e^lse_cur); o = e^(lse_prev - L) o_prev + e^(lse_cur - L) o_cur
-            // (the across-rounds accumulation of Ring attention).  lse_prev = -inf holds no
-            // keys: its o_prev is not read.
-            const float lp = lse_prev[lidx];
-            if (lp != -INFINITY) {
-                const float mx = fmaxf(lp, lse_cur);
-                const float ep = __expf(lp - mx), ec = __expf(lse_cur - mx);
-                const float inv = 1.0f / (ep + ec);
-                w_prev = ep * inv;
-                w_cur *= ec * inv;
-                lse_out = mx + __logf(ep + ec);
-            }
+    // Key tiles [lo, hi) of the current query tile, continuing the running state.
+    auto run = [&](int lo, int hi) {
+        const bool has_tail = hi == work.n_kv && Nkv % kBlockN != 0;  // the ragged last tile
+        const int n_full = (has_tail ? hi - 1 : hi) - lo;
+        if (n_full > 0) load_full(lo * kBlockN); else load_partial(lo * kBlockN);
+        store_tile(lo & 1);
+        __syncthreads();
+        int it = lo;
+        for (; it + 1 < lo + n_full; ++it) step(PF1{}, NOMASK{}, it);
+        if (n_full > 0) {
+            if (has_tail) step(PF2{}, NOMASK{}, it);
+            else step(PF0{}, NOMASK{}, it);
+            ++it;
         }
-        const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;
+        if (has_tail) step(PF0{}, MASKED{}, it);
+    };
+
+    // Sets the coordinates of query tile `tile`, loads its Q^T fragments (held for the
+    // whole key loop) and clears the running state.
+    auto begin_tile = [&](int tile) {
+        const int qt = tile % n_qtiles;
+        const int bh = tile / n_qtiles;
+        h = bh % H;
+        b = bh / H;
+        kbase = k + ((long)b * Nkv * H + h) * D;
+        vbase = v + ((long)b * Nkv * H + h) * D;
+        qrow = qt * kBlockM + wave * 32 + r;
+        const uint16_t* qp = q + (((long)b * Nq + qrow) * H + h) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : zero4;
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const long off = obase + db * 32 + 8 * i4;
-                f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
-                           acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
-                if constexpr (ACCUM) {
-                    if (w_prev != 0.0f) x += w_prev * *reinterpret_cast<const f32x4*>(o_prev + off);
-                }
-                if constexpr (OUT_F32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
-                } else {
-                    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) =
-                        __builtin_convertvector(x, bf16x4);
+            for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+        m_run = -INFINITY;
+        l_run = 0.f;
+    };
+
+    // O = acc / l and LSE = m + log2(l) (natural log of the scaled logits), or with ACCUM
+    // the combination with the previous result.
+    auto finish_tile = [&]() {
+        const float l_tot = halves_sum(l_run);
+        if (qrow < Nq) {
+            const long lidx = ((long)b * H + h) * Nq + qrow;
+            const float lse_cur = (m_run + log2f(l_tot)) * 0.693147180559945309f;
+            float w_cur = 1.0f / l_tot, w_prev = 0.0f, lse_out = lse_cur;
+            if constexpr (ACCUM) {
+                // L = ln(e^lse_prev + e^lse_cur); o = e^(lse_prev - L) o_prev + e^(lse_cur - L) o_cur
+                // (the across-rounds accumulation of Ring attention).  lse_prev = -inf holds no
+                // keys: its o_prev is not read.
+                const float lp = lse_prev[lidx];
+                if (lp != -INFINITY) {
+                    const float mx = fmaxf(lp, lse_cur);
+                    const float ep = __expf(lp - mx), ec = __expf(lse_cur - mx);
+                    const float inv = 1.0f / (ep + ec);
+                    w_prev = ep * inv;
+                    w_cur *= ec * inv;
+                    lse_out = mx + __logf(ep + ec);
                 }
             }
-        if (g == 0) lse[lidx] = lse_out;
+            const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const long off = obase + db * 32 + 8 * i4;
+                    f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
+                               acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
+                    if constexpr (ACCUM) {
+                        if (w_prev != 0.0f) x += w_prev * *reinterpret_cast<const f32x4*>(o_prev + off);
+                    }
+                    if constexpr (OUT_F32) {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
+                    } else {
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) =
+                            __builtin_convertvector(x, bf16x4);
+                    }
+                }
+            if (g == 0) lse[lidx] = lse_out;
+        }
+    };
+
+    if constexpr (!SPLIT) {
+        // one whole tile per workgroup, XCD-contiguous
+        begin_tile(xcd_contiguous(blockIdx.x, (int)gridDim.x) + tile_base);
+        run(0, work.n_kv);
+        finish_tile();
+        return;
+    } else {
+        // The workspace is written and read with system-scope (write-through, uncached)
+        // accesses, so no cache maintenance is needed: once a workgroup's stores have
+        // completed they are in memory, where every XCD reads them.
+        const int wg = xcd_contiguous(blockIdx.x, work.G_sk);
+        long u = sk_first_unit(work, wg);
+        const long u_end = sk_first_unit(work, wg + 1);
+        while (u < u_end) {
+            const int st = (int)(u / work.n_kv);
+            const long tile_u0 = (long)st * work.n_kv;
+            const int lo = (int)(u - tile_u0);
+            const int hi = (int)((u_end < tile_u0 + work.n_kv ? u_end : tile_u0 + work.n_kv) - tile_u0);
+            u = tile_u0 + hi;
+            begin_tile(tile_base + st);
+            // one run of key tiles per pass; a finaliser whose helpers have not published
+            // in time takes a second pass over the rest of the tile
+            int seg_lo = lo, seg_hi = hi;
+            bool publish = false;
+            for (;;) {
+                run(seg_lo, seg_hi);
+                if (lo > 0) { publish = true; break; }
+                if (seg_hi == work.n_kv) break;
+                // the tile's finaliser: fold in the states of the owners of keys [hi, n_kv)
+                const int g_first = sk_owner(work, tile_u0 + hi);
+                const int g_last = sk_owner(work, tile_u0 + work.n_kv - 1);
+                if (tid == 0) {
+                    // the helpers run concurrently and finish their pieces about now: poll,
+                    // but only for a bounded time
+                    int ok = 0;
+                    for (int poll = 0; poll < kMaxPolls && !ok; ++poll) {
+                        ok = 1;
+                        for (int gg = g_first; gg <= g_last; ++gg)
+                            ok &= __hip_atomic_load(work.flag + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == work.epoch;
+                        if (!ok) __builtin_amdgcn_s_sleep(8);
+                    }
+                    s_ready = ok;
+                }
+                __syncthreads();
+                const bool ready = s_ready != 0;
+                __syncthreads();   // s_ready is rewritten by the next finaliser check
+                if (!ready) {      // not published in time: compute the rest here
+                    seg_lo = seg_hi;
+                    seg_hi = work.n_kv;
+                    continue;
+                }
+                for (int gg = g_first; gg <= g_last; ++gg) {
+                    const float* wa = work.ws_acc + ((long)gg * kThreads + wave * 64) * (D / 2) + lane * 4;
+                    const f32x4 ml = load_sys<0>(work.ws_ml + ((long)gg * kThreads + tid) * 4);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    const float m_new = fmaxf(m_run, ml[0]);
+                    const float f_own = __builtin_amdgcn_exp2f(m_run - m_new);
+                    const float f_oth = __builtin_amdgcn_exp2f(ml[0] - m_new);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {   // one 32-column block at a time
+                        const float* wb = wa + db * 1024;
+                        f32x4 x[4];
+                        x[0] = load_sys<0>(wb);
+                        x[1] = load_sys<1024>(wb);
+                        x[2] = load_sys<2048>(wb);
+                        x[3] = load_sys<3072>(wb);
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            acc[db][i] = acc[db][i] * f_own + x[i / 4][i % 4] * f_oth;
+                    }
+                    l_run = l_run * f_own + ml[1] * f_oth;
+                    m_run = m_new;
+                }
+                break;
+            }
+            if (publish) {
+                // not the tile's first keys: hand the raw state to the tile's finaliser
+                // slot layout [wave][store j][lane][4]: each store instruction writes 1 KB
+                float* wa = work.ws_acc + ((long)wg * kThreads + wave * 64) * (D / 2) + lane * 4;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    float* wb = wa + db * 1024;   // 4 stores of 1 KB from here
+                    store_sys<0>(wb, __builtin_shufflevector(acc[db], acc[db], 0, 1, 2, 3));
+                    store_sys<1024>(wb, __builtin_shufflevector(acc[db], acc[db], 4, 5, 6, 7));
+                    store_sys<2048>(wb, __builtin_shufflevector(acc[db], acc[db], 8, 9, 10, 11));
+                    store_sys<3072>(wb, __builtin_shufflevector(acc[db], acc[db], 12, 13, 14, 15));
+                }
+                const f32x4 ml = {m_run, l_run, 0.f, 0.f};
+                store_sys<0>(work.ws_ml + ((long)wg * kThreads + tid) * 4, ml);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are done
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(work.flag + wg, work.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                continue;
+            }
+            finish_tile();
+        }
     }
 }
 
-template <int D, bool OUT_F32, bool ACCUM>
+template <int D, bool OUT_F32, bool ACCUM, bool SPLIT>
 void launch_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
                 const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
-                float scale_log2, int n_qtiles, int total, hipStream_t stream) {
-    attn_fwd_kernel<D, OUT_F32, ACCUM><<<dim3(total), dim3(kThreads), 0, stream>>>(
-        q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total);
+                float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
+                hipStream_t stream) {
+    attn_fwd_kernel<D, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(kThreads), 0, stream>>>(
+        q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, tile_base, work);
 }
 
-template <int D>
+template <int D, bool SPLIT>
 void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
               const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
-              float scale_log2, int n_qtiles, int total, bool out_f32, hipStream_t stream) {
+              float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
+              bool out_f32, hipStream_t stream) {
     const bool accum = o_prev != nullptr;
     if (out_f32) {
-        if (accum) launch_one<D, true, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
-        else launch_one<D, true, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
+        if (accum) launch_one<D, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
     } else {
-        if (accum) launch_one<D, false, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
-        else launch_one<D, false, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, stream);
+        if (accum) launch_one<D, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
     }
+}
+
+// Per-device launch facts: resident workgroups (2 per CU) and a memory pool for the
+// stream-ordered workspace.
+struct DeviceInfo {
+    int slots = 0;
+    hipMemPool_t pool = nullptr;
+};
+
+hipError_t device_info(DeviceInfo** out) {
+    static std::mutex mu;
+    static DeviceInfo infos[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    DeviceInfo& d = infos[dev];
+    if (d.slots == 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        e = hipMemPoolCreate(&d.pool, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;   // keep freed workspace in the pool for the next call
+        e = hipMemPoolSetAttribute(d.pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return e;
+        d.slots = 2 * cus;
+    }
+    *out = &d;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -410,17 +585,75 @@ void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
                            int H, int D, float scale, bool out_f32, hipStream_t stream) {
+    DeviceInfo* dev = nullptr;
+    hipError_t e = device_info(&dev);
+    if (e != hipSuccess) return e;
+    // DTL_ATTN_SLOTS (tests, tuning) schedules as if the GPU held that many workgroups; it
+    // changes which tiles are split, never the result.  It may only lower the count.
+    long slots = dev->slots;
+    if (const char* env = getenv("DTL_ATTN_SLOTS")) {
+        const long want = strtol(env, nullptr, 10);
+        if (want > 0 && want < slots) slots = want;
+    }
     const int n_qtiles = (Nq + kBlockM - 1) / kBlockM;
-    const int total = n_qtiles * H * B;  // the caller has checked that this fits an int
+    const long tiles = (long)n_qtiles * H * B;   // the caller has checked that this fits an int
+    StreamK work = {};
+    work.n_kv = (Nkv + kBlockN - 1) / kBlockN;
+    // Split the remainder only when it is a small part of a round of long tiles.  A larger
+    // remainder already runs well as whole tiles: with fewer workgroups than slots many
+    // CUs hold a single workgroup, whose waves then run faster (measured: 1.2x per
+    // workgroup), while every split piece pays a pipeline start, a publish and a merge, and
+    // the split part a second launch; with few key blocks per tile (cross-attention's 512
+    // keys) those costs exceed the idle tail they remove.
+    const long rem = tiles % slots;
+    const bool use_split = tiles >= slots && rem > 0 && rem * 4 <= slots &&
+                           (Nkv + kBlockN - 1) / kBlockN >= 64;
+    work.n_dp = (int)(use_split ? tiles - rem : tiles);   // a multiple of the slot count when split
+    const long W = (tiles - work.n_dp) * work.n_kv;         // units of the split part
+    work.G_sk = (int)(W < slots ? W : slots);
+    if (work.G_sk > 0) {
+        work.q = W / work.G_sk;
+        work.r = (int)(W % work.G_sk);
+    }
+    // a workspace is needed only when some split range starts inside a tile
+    bool split = false;
+    for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;
+    void* ws = nullptr;
+    if (split) {
+        static std::atomic<unsigned long long> epochs{0x9E3779B97F4A7C15ull};
+        const size_t acc_bytes = (size_t)work.G_sk * kThreads * (D / 2) * sizeof(float);
+        const size_t ml_bytes = (size_t)work.G_sk * kThreads * 4 * sizeof(float);
+        const size_t flag_bytes = (size_t)work.G_sk * sizeof(unsigned long long);
+        e = hipMallocFromPoolAsync(&ws, acc_bytes + ml_bytes + flag_bytes, dev->pool, stream);
+        if (e != hipSuccess) return e;
+        work.ws_acc = static_cast<float*>(ws);
+        work.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + acc_bytes);
+        work.flag = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + acc_bytes + ml_bytes);
+        work.epoch = epochs.fetch_add(1) + 1;
+    }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);
     auto qq = static_cast<const uint16_t*>(q);
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
-    if (D == 128)
-        launch_d<128>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, out_f32, stream);
-    else
-        launch_d<64>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, total, out_f32, stream);
-    return hipGetLastError();
+    // whole tiles first (complete rounds of the slots), then the split part
+    if (work.n_dp > 0) {
+        if (D == 128)
+            launch_d<128, false>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
+        else
+            launch_d<64, false>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
+    }
+    if (work.G_sk > 0) {
+        if (D == 128)
+            launch_d<128, true>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+        else
+            launch_d<64, true>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+    }
+    e = hipGetLastError();
+    if (ws != nullptr) {
+        const hipError_t f = hipFreeAsync(ws, stream);   // stream-ordered: after the kernel
+        if (e == hipSuccess) e = f;
+    }
+    return e;
 }
 
 }  // namespace dtl

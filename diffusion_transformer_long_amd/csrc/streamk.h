@@ -1,0 +1,54 @@
+// Stream-K work split of the attention kernel (also checked on the host).
+//
+// Tiles are 128-row query tiles ordered (batch, head) major, query tile minor.  With S
+// resident workgroup slots (two per CU), the first floor(tiles / S) * S tiles get one
+// workgroup each (n_dp of them, dispatched in order, XCD-contiguous so that the
+// workgroups of one XCD share a head's K/V in L2).  When the remaining tiles are few
+// (at most S/4) and long (at least 64 key blocks) they would leave most of the GPU idle
+// in a last round for a long time, so their work is
+// split evenly over G_sk workgroups of a second launch ("stream-K"): W units, a unit being one
+// 64-key block of one tile, and split workgroup g takes the contiguous units
+// [g*q + min(g, r), +q + (g < r)) with q = W / G_sk, r = W % G_sk.  Such a range is
+// processed as its pieces of consecutive tiles:
+//   whole tile                      -> final O and LSE
+//   piece starting inside a tile    -> the raw state (accumulators, reference max, row
+//     (only a range's first piece)     sum per lane) goes to workspace slot g, then flag[g]
+//                                      is set to this launch's epoch
+//   piece starting a tile, ending   -> the tile's finaliser: after its own keys it waits
+//     inside it (a range's last)       (bounded) for the flags of the workgroups that own
+//                                      the rest of the tile, folds in their states and
+//                                      writes O and LSE.
+// A finaliser only waits for split workgroups with higher ids, which are dispatched
+// after it and need nothing from anyone before publishing.  If a flag does not carry the
+// epoch within the bound, the finaliser computes the rest of the tile itself: the result
+// never depends on timing and every wave terminates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dtl {
+
+struct StreamK {
+    int n_dp;                   // whole-tile workgroups (tiles [0, n_dp))
+    int n_kv;                   // units (64-key blocks) per tile
+    int G_sk;                   // split workgroups (0: none)
+    long q;                     // split part: units per workgroup (W / G_sk)
+    int r;                      // split part: workgroups with one unit more (W % G_sk)
+    float* ws_acc;              // [G_sk][waves][D/8 stores][64 lanes][4] accumulators
+    float* ws_ml;               // [G_sk][threads][4] reference max, row-sum half, 2 unused
+    unsigned long long* flag;   // [G_sk]
+    unsigned long long epoch;   // this launch's flag value
+};
+
+// First unit of split-part workgroup g (g = G_sk gives W).
+__host__ __device__ __forceinline__ long sk_first_unit(const StreamK& w, int g) {
+    return (long)g * w.q + (g < w.r ? g : w.r);
+}
+
+// Workgroup that owns unit u < W.
+__host__ __device__ __forceinline__ int sk_owner(const StreamK& w, long u) {
+    const long big = (long)w.r * (w.q + 1);
+    return u < big ? (int)(u / (w.q + 1)) : w.r + (int)((u - big) / w.q);
+}
+
+}  // namespace dtl

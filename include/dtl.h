@@ -4,14 +4,22 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer owned by the caller (for example
- *     the storage of a torch tensor).  The library never allocates, frees, or keeps
- *     a pointer after the call returns.
+ *     the storage of a torch tensor).  The library keeps no pointer after the call
+ *     returns.  Only attn_fwd_lse and attn_fwd_lse_accumulate use memory of their own:
+ *     on workloads whose last round of tiles they split across the GPU (more 128-row
+ *     query tiles than twice the CU count, a remainder of at most a quarter of that,
+ *     and at least 4096 keys) they take a workspace of about 35 MB from a memory pool
+ *     the library creates per device, stream-ordered on `stream` (allocated before the
+ *     kernels, freed after them on the same stream).  The environment variable
+ *     DTL_ATTN_SLOTS, when set to a positive number below twice the CU count, makes
+ *     that choice as if the GPU held that many workgroups (for tests and tuning; the
+ *     result does not change).
  *   - Tensors are dense and row-major in the shapes given; there are no strides.
  *     Every pointer must be 16-byte aligned.
  *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.
  *   - Calls are asynchronous on `stream` (NULL selects the null stream).  They do
- *     not synchronize and hold no global state, so calls on different streams may
- *     run concurrently as long as their buffers do not overlap.
+ *     not synchronize, and every workspace belongs to one call, so calls on different
+ *     streams may run concurrently as long as their buffers do not overlap.
  *   - Arguments are validated on the host before anything is launched.  On a
  *     validation error nothing is launched and nothing is written.  DTL_ERR_HIP is
  *     returned when the kernel launch itself reports an error.  Device faults surface,
@@ -65,7 +73,8 @@ typedef enum {
  * weights are kept in f32 for the row sum and rounded to bf16 for the p.v product.
  * Errors: DTL_ERR_INVALID_ARG for null pointers, any size <= 0, a scale that is not
  * finite and positive, misaligned pointers, or an output overlapping an input or the
- * other output; DTL_ERR_UNSUPPORTED for D not in {64, 128} or another o_dtype.
+ * other output; DTL_ERR_UNSUPPORTED for D not in {64, 128} or another o_dtype;
+ * DTL_ERR_HIP when a launch or the workspace allocation fails.
  */
 dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
                         void *o, float *lse,

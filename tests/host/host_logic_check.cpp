@@ -1,6 +1,8 @@
 // Host-side checks of the index helpers the kernels use (built with hipcc, run on the CPU).
 //   fastdiv: FastDiv::div(n) == n / d for edge and random n, many d
 //   xcd:     xcd_contiguous is a bijection on [0, total) for many totals
+//   streamk: the attention's unit ranges partition [0, W) into G near-equal ranges and
+//            sk_owner inverts them
 //   runmap:  for the three permutes and many shapes, RunMap::source agrees with the
 //            element index map written out directly, stays in bounds and is a bijection
 #include <stdio.h>
@@ -11,6 +13,7 @@
 #include "common.h"
 #include "fastdiv.h"
 #include "runmap.h"
+#include "streamk.h"
 
 static uint64_t rng = 0x9E3779B97F4A7C15ull;
 static uint32_t next32() {  // xorshift64*
@@ -42,6 +45,23 @@ int main() {
             if (l < 0 || l >= total || seen[l]++) { if (bad < 10) printf("xcd total=%d pid=%d -> %d\n", total, pid, l); ++bad; }
         }
     }
+    const long Ws[] = {1, 2, 7, 63, 64, 511, 512, 513, 1000, 3888, 41088, 62208, 65537, 2193072};
+    const int Gs[] = {1, 2, 3, 7, 64, 216, 511, 512};
+    for (long W : Ws)
+        for (int G0 : Gs) {
+            dtl::StreamK w = {};
+            w.G_sk = (int)(W < G0 ? W : G0);
+            w.q = W / w.G_sk;
+            w.r = (int)(W % w.G_sk);
+            if (dtl::sk_first_unit(w, 0) != 0 || dtl::sk_first_unit(w, w.G_sk) != W) { printf("streamk ends W=%ld G=%d\n", W, w.G_sk); ++bad; }
+            for (int g = 0; g < w.G_sk; ++g) {
+                const long a = dtl::sk_first_unit(w, g), b = dtl::sk_first_unit(w, g + 1);
+                if (b - a != w.q + (g < w.r)) { if (bad < 10) printf("streamk size W=%ld G=%d g=%d\n", W, w.G_sk, g); ++bad; }
+                const long probes[] = {a, b - 1, (a + b) / 2};
+                for (long u : probes)
+                    if (dtl::sk_owner(w, u) != g) { if (bad < 10) printf("streamk owner W=%ld G=%d u=%ld\n", W, w.G_sk, u); ++bad; }
+            }
+        }
     // element source of output element o, written out from each map's definition
     auto direct = [](dtl::PermuteKind kind, long p, long B, long N, long H, long D, long o) -> long {
         const long Ns = N / p, Hs = H / p;

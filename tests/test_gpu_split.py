@@ -1,0 +1,111 @@
+"""GPU parity of the attention kernel's split ("stream-K") schedule.
+
+On the real GPU only large workloads reach it (more tiles than workgroup slots, a small
+remainder, at least 64 key blocks per tile: Wan2.2-5B).  DTL_ATTN_SLOTS schedules as if the
+GPU held fewer workgroups, which makes small shapes take the same path: whole tiles for
+the first rounds, the remainder's 64-key blocks spread over the slots, pieces published
+to the workspace and folded in by each tile's finaliser.  The cases cover a tile split
+over 8 workgroups, ranges crossing tile boundaries, the ragged last key block inside a
+split tile, B = 2, D = 64 and 128, bf16 and f32 outputs, and the accumulate entry point
+with rows that hold no keys yet.  Every result is compared with the oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import assert_close, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture
+def slots():
+    old = os.environ.get("DTL_ATTN_SLOTS")
+
+    def set_slots(n):
+        os.environ["DTL_ATTN_SLOTS"] = str(n)
+    yield set_slots
+    if old is None:
+        os.environ.pop("DTL_ATTN_SLOTS", None)
+    else:
+        os.environ["DTL_ATTN_SLOTS"] = old
+
+
+def _inputs(seed, B, Nq, Nkv, H, D, k_scale):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = synthetic.to_bf16(g.standard_normal((B, Nq, H, D), dtype=np.float32))
+    k = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32) * np.float32(k_scale))
+    v = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    return q, k, v
+
+
+CASES = [
+    # slots, B, Nq, Nkv, H, D, k_scale      tiles / remainder, key blocks
+    (8, 1, 1152, 4100, 1, 128, 1.0),       # 9 / 1, 65: one tile over 8 workgroups, ragged block
+    (8, 2, 300, 4097, 3, 64, 2.0),         # 18 / 2, 65: ranges cross tiles
+    (8, 1, 129, 64 * 66 + 7, 5, 128, 3.0),  # 10 / 2, 67
+    (4, 1, 640, 4096, 1, 128, 1.0),        # 5 / 1, 64: 4 workgroups of 16 blocks
+    (4, 1, 512, 4096, 1, 64, 1.0),         # 4 / 0: no split (control)
+    (8, 1, 1152, 1000, 1, 128, 1.0),       # 9 / 1, 16: too few key blocks to split (control)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "slots%d_B%d_Nq%d_Nkv%d_H%d_D%d" % c[:6])
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_split_schedule_matches_oracle(slots, case, o_dtype):
+    import diffusion_transformer_long_amd as dtl
+    n, B, Nq, Nkv, H, D, ks = case
+    log("split schedule slots=%d %s o=%s" % (n, case[1:], o_dtype))
+    q, k, v = _inputs(3000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
+    slots(n)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("O", to_np(o), o_ref)
+    assert_close("LSE", to_np(lse), l_ref)
+
+
+def test_split_schedule_accumulate(slots):
+    """attn_fwd_lse_accumulate through the split schedule, rows without previous keys."""
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Np, Nkv, H, D = 1, 1152, 300, 4100, 1, 128
+    g = np.random.Generator(np.random.PCG64(77))
+    q = synthetic.to_bf16(g.standard_normal((B, Nq, H, D), dtype=np.float32))
+    kp = synthetic.to_bf16(g.standard_normal((B, Np, H, D), dtype=np.float32))
+    vp = synthetic.to_bf16(g.standard_normal((B, Np, H, D), dtype=np.float32))
+    k = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    v = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    o_p, l_p = oracle.attn(q, kp, vp)
+    o_p32, l_p32 = o_p.astype(np.float32), l_p.astype(np.float32)
+    empty = np.arange(Nq) % 5 == 2
+    l_p32[:, :, empty] = -np.inf
+    o_p32[:, empty] = np.nan
+    o_c, l_c = oracle.attn(q, k, v)
+    o_ref, l_ref = oracle.merge(np.stack([np.nan_to_num(o_p32.astype(np.float64)), o_c]),
+                                np.stack([l_p32.astype(np.float64), l_c]))
+    slots(8)
+    o, lse = dtl.attn_fwd_lse_accumulate(q.to(DEV), k.to(DEV), v.to(DEV),
+                                         torch.from_numpy(o_p32).to(DEV), torch.from_numpy(l_p32).to(DEV))
+    torch.cuda.synchronize()
+    assert_close("O", to_np(o), o_ref)
+    assert_close("LSE", to_np(lse), l_ref)
+
+
+def test_split_schedule_repeated_calls_agree(slots):
+    """Back-to-back split launches (fresh epochs, reused pool memory) give one result."""
+    import diffusion_transformer_long_amd as dtl
+    q, k, v = _inputs(91, 1, 1152, 4100, 1, 128, 3.0)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    slots(8)
+    outs = [dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32) for _ in range(6)]
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(q, k, v)
+    for o, lse in outs:
+        assert_close("O", to_np(o), o_ref)
+        assert_close("LSE", to_np(lse), l_ref)
