@@ -103,18 +103,27 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 // System-scope (write-through, uncached) 16-byte accesses for the stream-K workspace: a
 // completed store is in memory, where a workgroup on any XCD reads it, so no cache
-// maintenance is needed.  The loads are not tracked by the compiler's wait counters: the
-// caller waits (vmcnt(0)) before using the results.
+// maintenance is needed.  A load statement issues its loads and waits for them itself,
+// so its outputs are valid when it ends (the compiler does not track these loads).
 // OFF is an immediate byte offset (< 4096) from p.
 template <int OFF>
 __device__ __forceinline__ void store_sys(float* p, f32x4 x) {
     asm volatile("global_store_dwordx4 %0, %1, off offset:%2 sc0 sc1" : : "v"(p), "v"(x), "i"(OFF) : "memory");
 }
-template <int OFF>
 __device__ __forceinline__ f32x4 load_sys(const float* p) {
     f32x4 x;
-    asm volatile("global_load_dwordx4 %0, %1, off offset:%2 sc0 sc1" : "=v"(x) : "v"(p), "i"(OFF) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(x) : "v"(p) : "memory");
     return x;
+}
+// four 16-byte loads at p, p + 1 KB, p + 2 KB, p + 3 KB
+__device__ __forceinline__ void load_sys4(const float* p, f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+    asm volatile("global_load_dwordx4 %0, %4, off sc0 sc1\n\t"
+                 "global_load_dwordx4 %1, %4, off offset:1024 sc0 sc1\n\t"
+                 "global_load_dwordx4 %2, %4, off offset:2048 sc0 sc1\n\t"
+                 "global_load_dwordx4 %3, %4, off offset:3072 sc0 sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d) : "v"(p) : "memory");
 }
 
 // ACCUM: continue from a previous result (o_prev, lse_prev) over other keys instead of
@@ -473,20 +482,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 }
                 for (int gg = g_first; gg <= g_last; ++gg) {
                     const float* wa = work.ws_acc + ((long)gg * kThreads + wave * 64) * (D / 2) + lane * 4;
-                    const f32x4 ml = load_sys<0>(work.ws_ml + ((long)gg * kThreads + tid) * 4);
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    const f32x4 ml = load_sys(work.ws_ml + ((long)gg * kThreads + tid) * 4);
                     const float m_new = fmaxf(m_run, ml[0]);
                     const float f_own = __builtin_amdgcn_exp2f(m_run - m_new);
                     const float f_oth = __builtin_amdgcn_exp2f(ml[0] - m_new);
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {   // one 32-column block at a time
-                        const float* wb = wa + db * 1024;
                         f32x4 x[4];
-                        x[0] = load_sys<0>(wb);
-                        x[1] = load_sys<1024>(wb);
-                        x[2] = load_sys<2048>(wb);
-                        x[3] = load_sys<3072>(wb);
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        load_sys4(wa + db * 1024, x[0], x[1], x[2], x[3]);
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
                             acc[db][i] = acc[db][i] * f_own + x[i / 4][i % 4] * f_oth;
