@@ -60,13 +60,13 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;   // query rows per workgroup
 constexpr int kBlockN = 64;            // keys per iteration
 // The running max moves only when a tile half raises it by more than this (log2 units).
-// A larger threshold skips more accumulator rescales, but then the dominant weight of a
-// peaked row is exp2(x) with x in (0, threshold] instead of exactly 1; at FLUX-like
-// logits (std 3) a threshold of 8 with an f32 row sum roughly triples the worst-case
-// error.  2 keeps the error near that of the exact-max scheme while rescaling about a
-// third of the tiles at N=4608 and 3% at N=27280.
+// A larger threshold skips more accumulator rescales; the dominant weight of a peaked row
+// is then exp2(x) with x in (0, threshold] instead of exactly 1, whose bf16 rounding the
+// rounded-weight row sum below cancels (with an f32 row sum a threshold of 8 would triple
+// the worst-case error at FLUX-like logits, std 3).  Weights stay below 2^8, well inside
+// the range of bf16 and of the f32 accumulators.
 #ifndef DTL_RESCALE_THRESHOLD
-#define DTL_RESCALE_THRESHOLD 2.0f
+#define DTL_RESCALE_THRESHOLD 8.0f
 #endif
 constexpr float kRescaleThreshold = DTL_RESCALE_THRESHOLD;
 // A tile's finaliser polls its helpers' flags at most this often (s_sleep 8 between
