@@ -600,24 +600,13 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     }
     const int n_qtiles = (Nq + kBlockM - 1) / kBlockM;
     const long tiles = (long)n_qtiles * H * B;   // the caller has checked that this fits an int
-    StreamK work = {};
-    work.n_kv = (Nkv + kBlockN - 1) / kBlockN;
-    // Split the remainder only when it is a small part of a round of long tiles.  A larger
+    // Split only where whole tiles would leave most of the GPU idle (streamk.h).  A larger
     // remainder already runs well as whole tiles: with fewer workgroups than slots many
     // CUs hold a single workgroup, whose waves then run faster (measured: 1.2x per
     // workgroup), while every split piece pays a pipeline start, a publish and a merge, and
     // the split part a second launch; with few key blocks per tile (cross-attention's 512
-    // keys) those costs exceed the idle tail they remove.
-    const long rem = tiles % slots;
-    const bool use_split = tiles >= slots && rem > 0 && rem * 4 <= slots &&
-                           (Nkv + kBlockN - 1) / kBlockN >= 64;
-    work.n_dp = (int)(use_split ? tiles - rem : tiles);   // a multiple of the slot count when split
-    const long W = (tiles - work.n_dp) * work.n_kv;         // units of the split part
-    work.G_sk = (int)(W < slots ? W : slots);
-    if (work.G_sk > 0) {
-        work.q = W / work.G_sk;
-        work.r = (int)(W % work.G_sk);
-    }
+    // keys) those costs exceed the idle tail.
+    StreamK work = plan_stream_k(tiles, (Nkv + kBlockN - 1) / kBlockN, slots);
     // a workspace is needed only when some split range starts inside a tile
     bool split = false;
     for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;

@@ -3,13 +3,15 @@
 // Tiles are 128-row query tiles ordered (batch, head) major, query tile minor.  With S
 // resident workgroup slots (two per CU), the first floor(tiles / S) * S tiles get one
 // workgroup each (n_dp of them, dispatched in order, XCD-contiguous so that the
-// workgroups of one XCD share a head's K/V in L2).  When the remaining tiles are few
-// (at most S/4) and long (at least 64 key blocks) they would leave most of the GPU idle
-// in a last round for a long time, so their work is
-// split evenly over G_sk workgroups of a second launch ("stream-K"): W units, a unit being one
-// 64-key block of one tile, and split workgroup g takes the contiguous units
-// [g*q + min(g, r), +q + (g < r)) with q = W / G_sk, r = W % G_sk.  Such a range is
-// processed as its pieces of consecutive tiles:
+// workgroups of one XCD share a head's K/V in L2).  When the remaining tiles are few (at
+// most S/4) and long (at least 64 key blocks) they would leave most of the GPU idle in a
+// last round for a long time, so their work is split evenly over G_sk workgroups of a
+// second launch ("stream-K", plan_stream_k): W units, a unit being one 64-key block of one
+// tile, and split workgroup g takes the contiguous units [g*q + min(g, r), +q + (g < r))
+// with q = W / G_sk, r = W % G_sk.  (A grid of fewer tiles than half the slots, such as a
+// Ring chunk of 1152 queries x 1152 keys, is not split: measured, pieces of 9 key blocks
+// ran 1.3x slower than whole tiles.)  Such a range is processed as its pieces of
+// consecutive tiles:
 //   whole tile                      -> final O and LSE
 //   piece starting inside a tile    -> the raw state (accumulators, reference max, row
 //     (only a range's first piece)     sum per lane) goes to workspace slot g, then flag[g]
@@ -43,6 +45,23 @@ struct StreamK {
 // First unit of split-part workgroup g (g = G_sk gives W).
 __host__ __device__ __forceinline__ long sk_first_unit(const StreamK& w, int g) {
     return (long)g * w.q + (g < w.r ? g : w.r);
+}
+
+// The schedule for `tiles` tiles of n_kv key blocks on `slots` workgroup slots: whole
+// tiles [0, n_dp), the rest split over G_sk workgroups (none when G_sk = 0).
+__host__ __device__ inline StreamK plan_stream_k(long tiles, int n_kv, long slots) {
+    StreamK w = {};
+    w.n_kv = n_kv;
+    const long rem = tiles % slots;
+    const bool split = tiles >= slots && rem > 0 && rem * 4 <= slots && n_kv >= 64;
+    w.n_dp = (int)(split ? tiles - rem : tiles);   // a multiple of the slot count when split
+    const long W = (tiles - w.n_dp) * n_kv;        // units of the split part
+    w.G_sk = (int)(W < slots ? W : slots);
+    if (w.G_sk > 0) {
+        w.q = W / w.G_sk;
+        w.r = (int)(W % w.G_sk);
+    }
+    return w;
 }
 
 // Workgroup that owns unit u < W.

@@ -2,7 +2,7 @@
 //   fastdiv: FastDiv::div(n) == n / d for edge and random n, many d
 //   xcd:     xcd_contiguous is a bijection on [0, total) for many totals
 //   streamk: the attention's unit ranges partition [0, W) into G near-equal ranges and
-//            sk_owner inverts them
+//            sk_owner inverts them; the schedule (plan_stream_k) splits only a short last round
 //   runmap:  for the three permutes and many shapes, RunMap::source agrees with the
 //            element index map written out directly, stays in bounds and is a bijection
 #include <stdio.h>
@@ -62,6 +62,33 @@ int main() {
                     if (dtl::sk_owner(w, u) != g) { if (bad < 10) printf("streamk owner W=%ld G=%d u=%ld\n", W, w.G_sk, u); ++bad; }
             }
         }
+    // the schedule: whole tiles first, the split part's ranges partition its units, at most
+    // one workgroup per slot, and the workloads land where intended
+    const long tiles_l[] = {1, 2, 9, 100, 216, 255, 256, 257, 300, 511, 512, 513, 600, 640, 864, 2955, 5120, 5136, 6000};
+    const int nkv_l[] = {1, 7, 8, 9, 16, 18, 63, 64, 65, 72, 148, 427, 1182};
+    const long slots_l[] = {4, 8, 64, 512};
+    for (long tiles : tiles_l)
+        for (int n_kv : nkv_l)
+            for (long slots : slots_l) {
+                const dtl::StreamK w = dtl::plan_stream_k(tiles, n_kv, slots);
+                const long W = (tiles - w.n_dp) * (long)n_kv;
+                const bool ok_dp = w.n_dp >= 0 && w.n_dp <= tiles && (W == 0) == (w.G_sk == 0);
+                bool ok = ok_dp && w.G_sk <= slots;
+                if (w.G_sk > 0)   // a short last round of long tiles
+                    ok = ok && w.q >= 1 && dtl::sk_first_unit(w, w.G_sk) == W && w.n_dp % slots == 0 &&
+                         n_kv >= 64 && (tiles - w.n_dp) * 4 <= slots;
+                if (!ok) { if (bad < 10) printf("plan tiles=%ld n_kv=%d slots=%ld -> n_dp=%d G=%d q=%ld\n", tiles, n_kv, slots, w.n_dp, w.G_sk, w.q); ++bad; }
+            }
+    {
+        const dtl::StreamK ring = dtl::plan_stream_k(216, 18, 512);     // FLUX Ring-4 chunk
+        const dtl::StreamK wan = dtl::plan_stream_k(5136, 427, 512);    // Wan2.2-5B
+        const dtl::StreamK flux = dtl::plan_stream_k(864, 72, 512);     // FLUX
+        const dtl::StreamK cross = dtl::plan_stream_k(5136, 8, 512);    // cross-attention
+        if (ring.G_sk != 0 || ring.n_dp != 216) { printf("plan ring\n"); ++bad; }
+        if (wan.n_dp != 5120 || wan.G_sk != 512) { printf("plan wan\n"); ++bad; }
+        if (flux.G_sk != 0 || flux.n_dp != 864) { printf("plan flux\n"); ++bad; }
+        if (cross.G_sk != 0 || cross.n_dp != 5136) { printf("plan cross\n"); ++bad; }
+    }
     // element source of output element o, written out from each map's definition
     auto direct = [](dtl::PermuteKind kind, long p, long B, long N, long H, long D, long o) -> long {
         const long Ns = N / p, Hs = H / p;
