@@ -139,9 +139,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int tile_base,
                      StreamK work) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBlockN * T::kRow];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * T::vRow];
+    // LDS: K tiles [2][64][D+8] and V^T tiles [2][D][64+8] (bf16) during the key loop; the
+    // output tile on its way to memory after it.
+    __shared__ __attribute__((aligned(16))) uint16_t s_lds[2 * kBlockN * T::kRow + 2 * D * T::vRow];
     __shared__ int s_ready;
+    auto sK = [&](int buf) { return s_lds + buf * (kBlockN * T::kRow); };
+    auto sV = [&](int buf) { return s_lds + 2 * kBlockN * T::kRow + buf * (D * T::vRow); };
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -212,7 +215,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < T::kChunks; ++c)
-            *reinterpret_cast<u32x4*>(&sK[buf][k_soff[c]]) = kreg[c];
+            *reinterpret_cast<u32x4*>(sK(buf) + k_soff[c]) = kreg[c];
         if (v_active) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -221,8 +224,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                             __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
                 u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
                             __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
-                *reinterpret_cast<u32x2*>(&sV[buf][v_soff + (2 * w) * T::vRow]) = lo;
-                *reinterpret_cast<u32x2*>(&sV[buf][v_soff + (2 * w + 1) * T::vRow]) = hi;
+                *reinterpret_cast<u32x2*>(sV(buf) + v_soff + (2 * w) * T::vRow) = lo;
+                *reinterpret_cast<u32x2*>(sV(buf) + v_soff + (2 * w + 1) * T::vRow) = hi;
             }
         }
     };
@@ -301,8 +304,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         if constexpr (PF == 1) load_full(kv0 + kBlockN);
         if constexpr (PF == 2) load_partial(kv0 + kBlockN);
 
-        const uint16_t* sk = sK[buf];
-        const uint16_t* sv = sV[buf];
+        const uint16_t* sk = sK(buf);
+        const uint16_t* sv = sV(buf);
         f32x16 s0, s1;
         bf16x8 p0[2], p1[2];
         float ls0, ls1, a0, a1;
@@ -386,13 +389,28 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     };
 
     // O = acc / l and LSE = m + log2(l) (natural log of the scaled logits), or with ACCUM
-    // the combination with the previous result.
+    // the combination with the previous result.  O goes out through LDS, which the key
+    // loop no longer needs: each lane leaves its 4-column pieces of its row there, then
+    // every store instruction writes whole rows (16 bytes per thread, consecutive threads
+    // along a row) instead of 8- or 16-byte pieces of 32 rows.  With ACCUM the tile is
+    // staged in f32, so that the combination rounds once.
     auto finish_tile = [&]() {
+        constexpr bool STAGE_F32 = OUT_F32 || ACCUM;
+        constexpr int ES = STAGE_F32 ? 4 : 2;            // staged element bytes
+        constexpr int RS = D * ES + 16;                  // staged row stride (bytes), padded
+        constexpr int OES = OUT_F32 ? 4 : 2;             // output element bytes
+        constexpr int EPC = 16 / OES;                    // output elements per 16-byte chunk
+        constexpr int CPR = D / EPC;                     // chunks per row
+        static_assert(kBlockM * RS + kBlockM * 4 <= (int)sizeof(s_lds), "output tile fits in LDS");
+        char* st = reinterpret_cast<char*>(s_lds);
+        float* s_wprev = reinterpret_cast<float*>(st + kBlockM * RS);
+        const int lrow = wave * 32 + r;                  // this lane's row in the tile
         const float l_tot = halves_sum(l_run);
+        float w_cur = 1.0f / l_tot, w_prev = 0.0f;
         if (qrow < Nq) {
             const long lidx = ((long)b * H + h) * Nq + qrow;
             const float lse_cur = (m_run + log2f(l_tot)) * 0.693147180559945309f;
-            float w_cur = 1.0f / l_tot, w_prev = 0.0f, lse_out = lse_cur;
+            float lse_out = lse_cur;
             if constexpr (ACCUM) {
                 // L = ln(e^lse_prev + e^lse_cur); o = e^(lse_prev - L) o_prev + e^(lse_cur - L) o_cur
                 // (the across-rounds accumulation of Ring attention).  lse_prev = -inf holds no
@@ -407,26 +425,52 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     lse_out = mx + __logf(ep + ec);
                 }
             }
-            const long obase = (((long)b * Nq + qrow) * H + h) * D + 4 * g;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const long off = obase + db * 32 + 8 * i4;
-                    f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
-                               acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
-                    if constexpr (ACCUM) {
-                        if (w_prev != 0.0f) x += w_prev * *reinterpret_cast<const f32x4*>(o_prev + off);
-                    }
-                    if constexpr (OUT_F32) {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
-                    } else {
-                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + off) =
-                            __builtin_convertvector(x, bf16x4);
-                    }
-                }
             if (g == 0) lse[lidx] = lse_out;
         }
+        // the key loop's last step ended with a barrier: LDS is free
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
+                                 acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
+                char* dst = st + lrow * RS + (db * 32 + 8 * i4 + 4 * g) * ES;
+                if constexpr (STAGE_F32) *reinterpret_cast<f32x4*>(dst) = x;
+                else *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(x, bf16x4);
+            }
+        if constexpr (ACCUM) {
+            if (g == 0) s_wprev[lrow] = w_prev;
+        }
+        __syncthreads();
+        const int row0 = qrow - lrow;                    // the tile's first query row
+#pragma unroll 4
+        for (int idx = tid; idx < kBlockM * CPR; idx += kThreads) {
+            const int row = idx / CPR, c = idx - (idx / CPR) * CPR;
+            if (row0 + row >= Nq) continue;
+            const long off = (((long)b * Nq + row0 + row) * H + h) * D + c * EPC;   // elements
+            const char* src = st + row * RS + c * EPC * ES;
+            if constexpr (!STAGE_F32) {
+                *reinterpret_cast<u32x4*>(static_cast<__bf16*>(o) + off) = *reinterpret_cast<const u32x4*>(src);
+            } else if constexpr (OUT_F32) {
+                f32x4 x = *reinterpret_cast<const f32x4*>(src);
+                if constexpr (ACCUM) {
+                    const float wp = s_wprev[row];
+                    if (wp != 0.0f) x += wp * *reinterpret_cast<const f32x4*>(o_prev + off);
+                }
+                *reinterpret_cast<f32x4*>(static_cast<float*>(o) + off) = x;
+            } else {   // ACCUM into a bf16 output: 8 values per chunk
+                f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+                f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 16);
+                const float wp = s_wprev[row];
+                if (wp != 0.0f) {
+                    x0 += wp * *reinterpret_cast<const f32x4*>(o_prev + off);
+                    x1 += wp * *reinterpret_cast<const f32x4*>(o_prev + off + 4);
+                }
+                const f32x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+                *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(o) + off) = __builtin_convertvector(x, bf16x8);
+            }
+        }
+        __syncthreads();   // LDS holds key tiles again after this
     };
 
     if constexpr (!SPLIT) {
