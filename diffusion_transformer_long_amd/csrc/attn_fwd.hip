@@ -23,8 +23,8 @@
 //                 matches them once K rows are stored in LDS in a permuted order (rows
 //                 m and sigma(m) swap bits 2 and 3), so that register i of lane l holds
 //                 key 16*(i/8) + 8*(l/32) + i%8 of its 32-key block.  A = V^T needs 8
-//                 consecutive keys of one head_dim column per lane, so V is transposed
-//                 on its way into LDS (4 keys x 8 columns per thread, in registers).
+//                 consecutive keys of one head_dim column per lane: V stays key-major in
+//                 LDS and two transposing reads (ds_read_b64_tr_b16) build it.
 //   The O^T accumulator also keeps one query per lane, so the softmax rescale is a
 //   per-lane scalar.
 //
@@ -42,8 +42,12 @@
 // tile), since a wave issues in order and VALU work only overlaps an MFMA when it sits
 // between MFMAs in the instruction stream.
 //
-// Full key tiles load without bounds checks from a uniform tile base plus per-thread
-// offsets fixed for the whole loop; only the ragged last tile is predicated and masked.
+// K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4: each
+// lane of an instruction fills 16 bytes of a 1 KB block; its source address picks the
+// piece), so staging takes no registers and no VALU work.  The layout (XOR-swizzled 16-byte
+// chunks, conflict-free reads) is in tile_layout.h.  Full tiles load without bounds checks
+// from a uniform tile base plus per-lane offsets fixed for the whole loop; the ragged last
+// tile repeats its last key for rows past the end (finite values whose logits are masked).
 #include <atomic>
 #include <cstdlib>
 #include <mutex>
@@ -51,6 +55,7 @@
 
 #include "common.h"
 #include "streamk.h"
+#include "tile_layout.h"
 
 namespace dtl {
 namespace {
@@ -75,21 +80,6 @@ constexpr int kMaxPolls = 20000;
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-template <int D>
-struct Tile {
-    static constexpr int kRow = D + 8;           // K row stride in LDS (bf16 units, +16 B pad)
-    static constexpr int vRow = kBlockN + 8;     // V^T row stride in LDS (bf16 units, +16 B pad)
-    static constexpr int kChunks = kBlockN * D / 8 / kThreads;  // 16-B K chunks per thread
-    static constexpr int vBlocks = (kBlockN / 4) * (D / 8);     // 4-key x 8-column V blocks
-    static constexpr int vPerThread = (vBlocks + kThreads - 1) / kThreads;
-    static_assert(kBlockN * D / 8 % kThreads == 0, "K tile must split evenly");
-};
-
-// LDS row of key `key` of a tile: bits 2 and 3 swapped (an involution).
-__device__ __forceinline__ int krow_slot(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-
 // max over the two lane halves (lanes l and l^32 hold the two halves of one query row)
 __device__ __forceinline__ float halves_max(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -99,6 +89,36 @@ __device__ __forceinline__ float halves_max(float x) {
 __device__ __forceinline__ float halves_sum(float x) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// One 1 KB global -> LDS load: lane i's 16 bytes at sbase + voff land at LDS byte address
+// lds + 16i.  Issued from inline assembly, so the compiler neither counts it nor waits for
+// it; the kernel waits (vmcnt) before the barrier that publishes a tile.  M0 carries the
+// LDS address and needs one wait state before the load.  sbase and lds are wave-uniform.
+// M0 is a reserved register; these kernels use it nowhere else (each statement sets it
+// right before its load), so the clobber only keeps the compiler from assuming it intact.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+    // readfirstlane returns int: widen through uint32_t, never by sign extension
+    const uint64_t a = reinterpret_cast<uint64_t>(sbase);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const char* base = reinterpret_cast<const char*>(((uint64_t)hi << 32) | (uint64_t)lo);
+    const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read: each 16 lanes read a 4-row x 16-column block of 16-bit elements;
+// lane L supplies the address of row (L%16)/4, columns 4(L%4)..4(L%4)+3, and receives
+// column L%16, rows 0..3.
+__device__ __forceinline__ bf16x4 read_tr(const LDS_AS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
 }
 
 // System-scope (write-through, uncached) 16-byte accesses for the stream-K workspace: a
@@ -138,97 +158,69 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      const float* o_prev, const float* lse_prev,
                      int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int tile_base,
                      StreamK work) {
-    using T = Tile<D>;
-    // LDS: K tiles [2][64][D+8] and V^T tiles [2][D][64+8] (bf16) during the key loop; the
-    // output tile on its way to memory after it.
-    __shared__ __attribute__((aligned(16))) uint16_t s_lds[2 * kBlockN * T::kRow + 2 * D * T::vRow];
+    using L = TileLayout<D>;
+    // LDS: K and V tiles, two buffers each ([K0 | K1 | V0 | V1], key-major, layout in
+    // TileLayout) during the key loop; the output tile on its way to memory after it.
+    constexpr int kStageBytes = kBlockM * (4 * D + 16) + kBlockM * 4;   // f32 output staging
+    constexpr int kLdsBytes = 4 * L::kTileBytes > kStageBytes ? 4 * L::kTileBytes : kStageBytes;
+    __shared__ __attribute__((aligned(16))) char s_lds[kLdsBytes];
     __shared__ int s_ready;
-    auto sK = [&](int buf) { return s_lds + buf * (kBlockN * T::kRow); };
-    auto sV = [&](int buf) { return s_lds + 2 * kBlockN * T::kRow + buf * (D * T::vRow); };
+    auto sK = [&](int buf) { return s_lds + buf * L::kTileBytes; };
+    auto sV = [&](int buf) { return s_lds + (2 + buf) * L::kTileBytes; };
+    auto lds_addr = [&](const char* p) { return (uint32_t)(size_t)(const LDS_AS void*)p; };
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int g = lane >> 5;   // lane half
     const int r = lane & 31;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     const int tok_stride = H * D;  // elements between consecutive tokens (H*D <= 2^24, checked on the host)
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const long ts_bytes = 2L * tok_stride;
 
-    // Per-thread tile geometry, fixed for the whole kernel.
-    //   K: chunk c covers key row k_row[c] and 8 columns; it lands in LDS row krow_slot(k_row[c]).
-    //   V: a block of 4 keys (vk0..vk0+3) x 8 columns (vd0..vd0+7), stored transposed.
-    int k_goff[T::kChunks], k_soff[T::kChunks], k_row[T::kChunks];
+    // Per-lane load offsets (bytes from a tile's first key), fixed for the whole kernel:
+    // load instruction i of this wave fetches the piece TileLayout assigns to this lane.
+    // A tile spans 64 * ts_bytes < 2^31 bytes, so they fit 32 bits.
+    constexpr int NL = L::kLoadsPerWave;
+    uint32_t k_src[NL], v_src[NL];
 #pragma unroll
-    for (int c = 0; c < T::kChunks; ++c) {
-        const int idx = tid + c * kThreads;
-        const int row = idx / (D / 8), col = idx % (D / 8);
-        k_row[c] = row;
-        k_goff[c] = row * tok_stride + col * 8;
-        k_soff[c] = krow_slot(row) * T::kRow + col * 8;
+    for (int i = 0; i < NL; ++i) {
+        k_src[i] = (uint32_t)(L::k_src_key(wave, i, lane) * ts_bytes + 16 * L::k_src_chunk(wave, i, lane));
+        v_src[i] = (uint32_t)(L::v_src_key(wave, i, lane) * ts_bytes + 16 * L::v_src_chunk(wave, i, lane));
     }
-    const bool v_active = T::vBlocks >= kThreads || tid < T::vBlocks;
-    const int vk0 = (tid % (kBlockN / 4)) * 4;
-    const int vd0 = (tid / (kBlockN / 4)) * 8;
-    const int v_goff = vk0 * tok_stride + vd0;
-    const int v_soff = vd0 * T::vRow + vk0;
-    static_assert(T::vPerThread == 1, "one V block per thread");
 
     // the current tile's coordinates and state
     const uint16_t* kbase = k;
     const uint16_t* vbase = v;
     int b = 0, h = 0, qrow = 0;
     bf16x8 qf[D / 16];
-    u32x4 kreg[T::kChunks];
-    u32x4 vreg[4];
     f32x16 acc[D / 32];
     float m_run;   // reference max of this lane's query row (log2 units)
     float l_run;   // this lane's half of the row sum, relative to m_run
 
-    // Global -> registers for the tile starting at key kv0.  A full tile needs no checks;
-    // the ragged last tile reads zeros past Nkv (its logits are masked below).
-    auto load_full = [&](int kv0) {
-        const uint16_t* kt = kbase + (long)kv0 * tok_stride;
-        const uint16_t* vt = vbase + (long)kv0 * tok_stride;
+    // Global -> LDS for the tile starting at key kv0 into buffer buf.  The ragged last tile
+    // repeats its last key for rows past Nkv (finite values: their logits are masked and
+    // their weights are 0).
+    auto load_tile = [&](auto partial_c, int kv0, int buf) {
+        constexpr bool PARTIAL = decltype(partial_c)::value;
+        const char* kt = reinterpret_cast<const char*>(kbase) + kv0 * ts_bytes;
+        const char* vt = reinterpret_cast<const char*>(vbase) + kv0 * ts_bytes;
+        const uint32_t kd = lds_addr(sK(buf)), vd = lds_addr(sV(buf));
+        const int last = Nkv - 1 - kv0;
 #pragma unroll
-        for (int c = 0; c < T::kChunks; ++c)
-            kreg[c] = *reinterpret_cast<const u32x4*>(kt + k_goff[c]);
-        if (v_active) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vreg[j] = *reinterpret_cast<const u32x4*>(vt + v_goff + j * tok_stride);
-        }
-    };
-    auto load_partial = [&](int kv0) {
-        const uint16_t* kt = kbase + (long)kv0 * tok_stride;
-        const uint16_t* vt = vbase + (long)kv0 * tok_stride;
-        const int nk = Nkv - kv0;
-#pragma unroll
-        for (int c = 0; c < T::kChunks; ++c)
-            kreg[c] = k_row[c] < nk ? *reinterpret_cast<const u32x4*>(kt + k_goff[c]) : zero4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            vreg[j] = (v_active && vk0 + j < nk)
-                ? *reinterpret_cast<const u32x4*>(vt + v_goff + j * tok_stride) : zero4;
-    };
-
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < T::kChunks; ++c)
-            *reinterpret_cast<u32x4*>(sK(buf) + k_soff[c]) = kreg[c];
-        if (v_active) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // column vd0+2w: low halves of the 4 keys; column vd0+2w+1: high halves
-                u32x2 lo = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u),
-                            __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
-                u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
-                            __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
-                *reinterpret_cast<u32x2*>(sV(buf) + v_soff + (2 * w) * T::vRow) = lo;
-                *reinterpret_cast<u32x2*>(sV(buf) + v_soff + (2 * w + 1) * T::vRow) = hi;
+        for (int i = 0; i < NL; ++i) {
+            uint32_t ko = k_src[i], vo = v_src[i];
+            if constexpr (PARTIAL) {
+                ko = (uint32_t)(min(L::k_src_key(wave, i, lane), last) * ts_bytes + 16 * L::k_src_chunk(wave, i, lane));
+                vo = (uint32_t)(min(L::v_src_key(wave, i, lane), last) * ts_bytes + 16 * L::v_src_chunk(wave, i, lane));
             }
+            dma16(kt, ko, kd + L::load_block(wave_u, i));
+            dma16(vt, vo, vd + L::load_block(wave_u, i));
         }
     };
+    using FULL = std::false_type;
+    using PARTIAL = std::true_type;
 
     // Online-softmax update for one 32-key half of a tile: moves the reference max when the
     // half raises it by more than kRescaleThreshold, then rounds exp2(s*c - m) to bf16 for the
@@ -268,22 +260,23 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     };
-    auto s_half = [&](f32x16& s, const uint16_t* sk, int kb) {
+    auto s_half = [&](f32x16& s, const LDS_AS char* sk, int kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + (kb * 32 + r) * T::kRow + ks * 16 + g * 8);
+            const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(sk + L::k_frag(kb, ks, lane));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
         }
     };
-    auto pv_half = [&](const bf16x8 (&pf)[2], const uint16_t* sv, int kb) {
+    auto pv_half = [&](const bf16x8 (&pf)[2], const LDS_AS char* sv, int kb) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    sv + (db * 32 + r) * T::vRow + kb * 32 + hf * 16 + g * 8);
+                const bf16x4 lo = read_tr(sv + L::v_frag(kb, hf, db, 0, lane));
+                const bf16x4 hi = read_tr(sv + L::v_frag(kb, hf, db, 1, lane));
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[hf], acc[db], 0, 0, 0);
             }
     };
@@ -301,11 +294,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         constexpr bool MASK = decltype(mask_c)::value;
         const int buf = it & 1;
         const int kv0 = it * kBlockN;
-        if constexpr (PF == 1) load_full(kv0 + kBlockN);
-        if constexpr (PF == 2) load_partial(kv0 + kBlockN);
+        // the next tile goes into the other buffer, which the previous step's barrier freed
+        if constexpr (PF == 1) load_tile(FULL{}, kv0 + kBlockN, buf ^ 1);
+        if constexpr (PF == 2) load_tile(PARTIAL{}, kv0 + kBlockN, buf ^ 1);
 
-        const uint16_t* sk = sK(buf);
-        const uint16_t* sv = sV(buf);
+        const LDS_AS char* sk = (const LDS_AS char*)(const LDS_AS void*)sK(buf);
+        const LDS_AS char* sv = (const LDS_AS char*)(const LDS_AS void*)sV(buf);
         f32x16 s0, s1;
         bf16x8 p0[2], p1[2];
         float ls0, ls1, a0, a1;
@@ -338,7 +332,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         l_run += ls0 * a1 + ls1;
         if (r1) rescale_acc(a1);
         pv_half(p1, sv, 1);
-        if constexpr (PF != 0) store_tile(buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);   // the P.V MFMAs issue before the wait
+        if constexpr (PF != 0) wait_dma();
         __syncthreads();
     };
     using PF0 = std::integral_constant<int, 0>;
@@ -351,8 +346,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     auto run = [&](int lo, int hi) {
         const bool has_tail = hi == work.n_kv && Nkv % kBlockN != 0;  // the ragged last tile
         const int n_full = (has_tail ? hi - 1 : hi) - lo;
-        if (n_full > 0) load_full(lo * kBlockN); else load_partial(lo * kBlockN);
-        store_tile(lo & 1);
+        if (n_full > 0) load_tile(FULL{}, lo * kBlockN, lo & 1);
+        else load_tile(PARTIAL{}, lo * kBlockN, lo & 1);
+        wait_dma();
+        // the Q loads are complete too: tell the compiler, which does not see the tile
+        // loads, so that it puts no wait for them inside the key loop
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         int it = lo;
         for (; it + 1 < lo + n_full; ++it) step(PF1{}, NOMASK{}, it);
@@ -377,7 +376,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const uint16_t* qp = q + (((long)b * Nq + qrow) * H + h) * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : zero4;
+            u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
 #pragma unroll
@@ -402,7 +401,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         constexpr int EPC = 16 / OES;                    // output elements per 16-byte chunk
         constexpr int CPR = D / EPC;                     // chunks per row
         static_assert(kBlockM * RS + kBlockM * 4 <= (int)sizeof(s_lds), "output tile fits in LDS");
-        char* st = reinterpret_cast<char*>(s_lds);
+        char* st = s_lds;
         float* s_wprev = reinterpret_cast<float*>(st + kBlockM * RS);
         const int lrow = wave * 32 + r;                  // this lane's row in the tile
         const float l_tot = halves_sum(l_run);

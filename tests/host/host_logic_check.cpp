@@ -5,6 +5,10 @@
 //            sk_owner inverts them; the schedule (plan_stream_k) splits only a short last round
 //   runmap:  for the three permutes and many shapes, RunMap::source agrees with the
 //            element index map written out directly, stays in bounds and is a bijection
+//   tile:    the attention's LDS key-tile layout (head_dim 64 and 128): the direct loads
+//            fill every row and chunk of a tile once, the K and V^T fragment reads (the
+//            latter through the transposing read's lane exchange) return exactly the
+//            elements the MFMA operands need, and no read has a bank conflict
 #include <stdio.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -14,11 +18,94 @@
 #include "fastdiv.h"
 #include "runmap.h"
 #include "streamk.h"
+#include "tile_layout.h"
 
 static uint64_t rng = 0x9E3779B97F4A7C15ull;
 static uint32_t next32() {  // xorshift64*
     rng ^= rng >> 12; rng ^= rng << 25; rng ^= rng >> 27;
     return (uint32_t)((rng * 2685821657736338717ull) >> 32);
+}
+
+// A tile in LDS as (key, 16-byte chunk) per 16-byte slot, filled by the load placement.
+template <int D>
+static long check_tile_layout() {
+    using L = dtl::TileLayout<D>;
+    long bad = 0;
+    auto fail = [&](const char* what, int a, int b, int c) {
+        if (bad < 10) printf("tile D=%d %s %d %d %d\n", D, what, a, b, c);
+        ++bad;
+    };
+    for (int tensor = 0; tensor < 2; ++tensor) {
+        const int slots = L::kTileBytes / 16;
+        std::vector<int> key_at(slots, -1), chunk_at(slots, -1), seen(slots, 0);
+        for (int w = 0; w < 4; ++w)
+            for (int i = 0; i < L::kLoadsPerWave; ++i)
+                for (int l = 0; l < 64; ++l) {
+                    const int byte = L::load_block(w, i) + 16 * l;
+                    if (byte != L::load_row(w, i, l) * L::kRowBytes + 16 * (l % L::kChunks)) fail("block", w, i, l);
+                    const int key = tensor ? L::v_src_key(w, i, l) : L::k_src_key(w, i, l);
+                    const int ch = tensor ? L::v_src_chunk(w, i, l) : L::k_src_chunk(w, i, l);
+                    if (byte < 0 || byte >= L::kTileBytes || key < 0 || key >= 64 || ch < 0 || ch >= L::kChunks) {
+                        fail("range", w, i, l);
+                        continue;
+                    }
+                    key_at[byte / 16] = key; chunk_at[byte / 16] = ch;
+                    ++seen[key * L::kChunks + ch];
+                }
+        for (int e = 0; e < slots; ++e)
+            if (seen[e] != 1) fail("fill", tensor, e, seen[e]);
+        if (tensor == 0) {
+            // The S^T = K Q^T accumulator of a 32x32 MFMA holds, in register i of lane l, output
+            // row 8 (i/4) + 4 (l/32) + i%4 (the A row, i.e. the LDS row within the key half);
+            // with the rows permuted by krow_slot that is key 16 (i/8) + 8 (l/32) + i%8, the
+            // order in which the P.V product takes its B operand.
+            for (int l = 0; l < 64; ++l)
+                for (int i = 0; i < 16; ++i)
+                    if (dtl::krow_slot(8 * (i / 4) + 4 * (l / 32) + i % 4) != 16 * (i / 8) + 8 * (l / 32) + i % 8)
+                        fail("kperm", l, i, 0);
+            // K: lane l of read (kb, ks) gets chunk 2 ks + l/32 of key krow_slot(kb*32 + l%32)
+            for (int kb = 0; kb < 2; ++kb)
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    std::vector<int> bank_used(16 * 4, 0);
+                    for (int l = 0; l < 64; ++l) {
+                        const int off = L::k_frag(kb, ks, l);
+                        if (off % 16 || off < 0 || off >= L::kTileBytes) { fail("kread", kb, ks, l); continue; }
+                        if (key_at[off / 16] != dtl::krow_slot(kb * 32 + (l & 31)) || chunk_at[off / 16] != 2 * ks + (l >> 5))
+                            fail("kfrag", kb, ks, l);
+                        // 16 lanes (256 bytes) per LDS cycle: their 16-byte bank groups must differ
+                        if (bank_used[(l / 16) * 16 + (off / 16) % 16]++) fail("kbank", kb, ks, l);
+                    }
+                }
+        } else {
+            // V^T: the transposing read gives lane l (in its 16-lane group G) element l%4 of
+            // the 8 bytes that lane 16G + 4 rho + (l%16)/4 addressed, for rho = 0..3; that must
+            // be V[key kb*32 + hf*16 + 8 (l/32) + 4 j + rho][column db*32 + l%32].
+            for (int kb = 0; kb < 2; ++kb)
+                for (int hf = 0; hf < 2; ++hf)
+                    for (int db = 0; db < D / 32; ++db)
+                        for (int j = 0; j < 2; ++j) {
+                            std::vector<int> bank_used(32 * 2, 0);
+                            for (int l = 0; l < 64; ++l) {
+                                const int off = L::v_frag(kb, hf, db, j, l);
+                                if (off % 8 || off < 0 || off >= L::kTileBytes) { fail("vread", kb, hf, l); continue; }
+                                // 32 lanes x 8 bytes per LDS cycle: distinct 8-byte bank pairs
+                                if (bank_used[(l / 32) * 32 + (off / 8) % 32]++) fail("vbank", kb, db, l);
+                            }
+                            for (int l = 0; l < 64; ++l) {
+                                const int G = l / 16;
+                                for (int rho = 0; rho < 4; ++rho) {
+                                    const int src_lane = 16 * G + 4 * rho + (l % 16) / 4;
+                                    const int off = L::v_frag(kb, hf, db, j, src_lane) + 2 * (l % 4);
+                                    const int key = key_at[off / 16];
+                                    const int col = 8 * chunk_at[off / 16] + (off % 16) / 2;
+                                    if (key != kb * 32 + hf * 16 + 8 * (l >> 5) + 4 * j + rho || col != db * 32 + (l & 31))
+                                        fail("vfrag", kb * 4 + hf * 2 + j, db, l);
+                                }
+                            }
+                        }
+        }
+    }
+    return bad;
 }
 
 int main() {
@@ -136,6 +223,8 @@ int main() {
                     }
                 }
             }
+    bad += check_tile_layout<128>();
+    bad += check_tile_layout<64>();
     printf("%s (%ld failures)\n", bad ? "FAIL" : "OK", bad);
     return bad ? 1 : 0;
 }
