@@ -43,7 +43,7 @@ PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 f
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_flux_N4608_H24_D128_pmc.txt")
 ATTN_SRCS = [os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc", f)
-             for f in ("attn_fwd.hip", "common.h", "streamk.h")] + \
+             for f in ("attn_fwd.hip", "common.h", "streamk.h", "tile_layout.h")] + \
             [os.path.join(ROOT, "diffusion_transformer_long_amd", "build.py")]   # its compile flags
 
 
