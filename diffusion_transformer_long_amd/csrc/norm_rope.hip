@@ -109,19 +109,20 @@ void qkv_norm_rope_kernel(const u32x4* __restrict__ in, const float* __restrict_
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)HD + eps);
     const float* gamma = c == 0 ? gamma_q : gamma_k;
-    const float* crow = cs + (long)t * (D / 2);
-    const float* srow = sn + (long)t * (D / 2);
+    // every chunk of a lane sits at the same place within its head (64 lanes x 8 elements
+    // are whole heads), so the lane's cos/sin values are the same for all its chunks
+    static_assert(512 % D == 0, "a wave's 512 elements are whole heads");
+    const int i0 = ((lane * 8) % D) / 2;           // first pair of the lane's chunks within a head
+    const f32x4 co = *reinterpret_cast<const f32x4*>(cs + (long)t * (D / 2) + i0);
+    const f32x4 si = *reinterpret_cast<const f32x4*>(sn + (long)t * (D / 2) + i0);
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
         const int ci = lane + 64 * k;
         if (ci < nch) {
             const int e0 = ci * 8;                 // first element (h*D + d0)
-            const int i0 = (e0 % D) / 2;           // first pair of the chunk within its head
             const f32x8 v = __builtin_convertvector(__builtin_bit_cast(bf16x8, x[k]), f32x8);
             const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + e0);
             const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + e0 + 4);
-            const f32x4 co = *reinterpret_cast<const f32x4*>(crow + i0);
-            const f32x4 si = *reinterpret_cast<const f32x4*>(srow + i0);
             const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
             f32x8 y;
 #pragma unroll
