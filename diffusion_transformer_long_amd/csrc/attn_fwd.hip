@@ -40,7 +40,7 @@
 // (S of key half 0; S of half 1 with the softmax of half 0; P.V of half 0 with the
 // softmax of half 1; P.V of half 1), since a wave issues in order and VALU work only
 // overlaps an MFMA when it sits between MFMAs in the instruction stream.  The loads of
-// the next tile are issued when a tile starts.
+// the next tile are issued after the first block.
 //
 // K and V tiles go from global memory straight into LDS (global_load_lds_dwordx4: each
 // lane of an instruction fills 16 bytes of a 1 KB block; its source address picks the
@@ -294,9 +294,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         constexpr bool MASK = decltype(mask_c)::value;
         const int buf = it & 1;
         const int kv0 = it * kBlockN;
-        // the next tile goes into the other buffer, which the previous step's barrier freed
-        if constexpr (PF == 1) load_tile(FULL{}, kv0 + kBlockN, buf ^ 1);
-        if constexpr (PF == 2) load_tile(PARTIAL{}, kv0 + kBlockN, buf ^ 1);
 
         const LDS_AS char* sk = (const LDS_AS char*)(const LDS_AS void*)sK(buf);
         const LDS_AS char* sv = (const LDS_AS char*)(const LDS_AS void*)sV(buf);
@@ -306,6 +303,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
         s_half(s0, sk, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // the next tile goes into the other buffer, which the previous step's barrier freed;
+        // issued after the first block's MFMAs rather than before them (0.5% faster at long
+        // key ranges, 4% at 512 keys)
+        if constexpr (PF == 1) load_tile(FULL{}, kv0 + kBlockN, buf ^ 1);
+        if constexpr (PF == 2) load_tile(PARTIAL{}, kv0 + kBlockN, buf ^ 1);
         // The two softmax blocks run at raised wave priority: when both waves of a SIMD can
         // issue, the one with VALU work goes first and the other's MFMAs fill the matrix
         // pipe behind it (measured 1-2% faster than equal priorities).
