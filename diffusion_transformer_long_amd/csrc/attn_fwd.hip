@@ -9,8 +9,8 @@
 // parallelism, section 4.2).
 //
 // Work decomposition
-//   workgroup = 4 waves = 128 query rows of one (batch, head); wave w owns rows
-//   [32w, 32w+32).  Keys are consumed 64 per iteration from a double-buffered LDS tile.
+//   workgroup = NW waves (4 or 8) = 32 NW query rows of one (batch, head); wave w owns
+//   rows [32w, 32w+32).  Keys are consumed 64 per iteration from a double-buffered LDS tile.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] B[16x32]):
 //   S^T = K Q^T:  A = a 32-key block of K (lane l: key row l%32, 8 head_dim values
@@ -60,9 +60,11 @@
 namespace dtl {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;   // query rows per workgroup
+// A workgroup has NW waves of 32 query rows (a 32 NW-row query tile): NW = 4, two
+// workgroups per CU, in general; NW = 8, one per CU, where the key range is long and the
+// 256-row tiles still fill the GPU, since every K/V tile then feeds twice the query rows
+// (measured 5.5% faster at FLUX N=4608, 1.6% at Wan2.2-5B, 2% at the Wan2.1-14B chunk, but
+// slower at 512 keys and at 1152 x 1152 Ring chunks, which keep NW = 4).
 constexpr int kBlockN = 64;            // keys per iteration
 // The running max moves only when a tile half raises it by more than this (log2 units).
 // A larger threshold skips more accumulator rescales; the dominant weight of a peaked row
@@ -151,14 +153,16 @@ __device__ __forceinline__ void load_sys4(const float* p, f32x4& a, f32x4& b, f3
 // element is read before it is written, by the same lane), so none of them is restrict.
 // SPLIT = false: one whole tile per workgroup, tiles [tile_base, tile_base + grid).
 // SPLIT = true: the split part, tiles from tile_base on, as stream-K unit ranges.
-template <int D, bool OUT_F32, bool ACCUM, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2)
+template <int D, int NW, bool OUT_F32, bool ACCUM, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 8 / NW)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, void* o, float* lse,
                      const float* o_prev, const float* lse_prev,
                      int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int tile_base,
                      StreamK work) {
-    using L = TileLayout<D>;
+    constexpr int kThreads = NW * 64;
+    constexpr int kBlockM = NW * 32;   // query rows per workgroup
+    using L = TileLayout<D, NW>;
     // LDS: K and V tiles, two buffers each ([K0 | K1 | V0 | V1], key-major, layout in
     // TileLayout) during the key loop; the output tile on its way to memory after it.
     constexpr int kStageBytes = kBlockM * (4 * D + 16) + kBlockM * 4;   // f32 output staging
@@ -574,34 +578,47 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, bool OUT_F32, bool ACCUM, bool SPLIT>
+template <int D, int NW, bool OUT_F32, bool ACCUM, bool SPLIT>
 void launch_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
                 const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
                 float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
                 hipStream_t stream) {
-    attn_fwd_kernel<D, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(kThreads), 0, stream>>>(
+    attn_fwd_kernel<D, NW, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
         q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, tile_base, work);
 }
 
-template <int D, bool SPLIT>
+template <int D, int NW, bool SPLIT>
 void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
               const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
               float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
               bool out_f32, hipStream_t stream) {
     const bool accum = o_prev != nullptr;
     if (out_f32) {
-        if (accum) launch_one<D, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
     } else {
-        if (accum) launch_one<D, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
     }
 }
 
-// Per-device launch facts: resident workgroups (2 per CU) and a memory pool for the
-// stream-ordered workspace.
+// the launches of one schedule: whole tiles first (complete rounds of the slots), then the
+// split part
+template <int D, int NW>
+void launch_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
+                     const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
+                     float scale_log2, int n_qtiles, const StreamK& work, bool out_f32,
+                     hipStream_t stream) {
+    if (work.n_dp > 0)
+        launch_d<D, NW, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
+    if (work.G_sk > 0)
+        launch_d<D, NW, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+}
+
+// Per-device launch facts: compute units and a memory pool for the stream-ordered
+// workspace.
 struct DeviceInfo {
-    int slots = 0;
+    int cus = 0;
     hipMemPool_t pool = nullptr;
 };
 
@@ -614,7 +631,7 @@ hipError_t device_info(DeviceInfo** out) {
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
     DeviceInfo& d = infos[dev];
-    if (d.slots == 0) {
+    if (d.cus == 0) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
@@ -627,7 +644,7 @@ hipError_t device_info(DeviceInfo** out) {
         uint64_t keep = UINT64_MAX;   // keep freed workspace in the pool for the next call
         e = hipMemPoolSetAttribute(d.pool, hipMemPoolAttrReleaseThreshold, &keep);
         if (e != hipSuccess) return e;
-        d.slots = 2 * cus;
+        d.cus = cus;
     }
     *out = &d;
     return hipSuccess;
@@ -643,12 +660,23 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     if (e != hipSuccess) return e;
     // DTL_ATTN_SLOTS (tests, tuning) schedules as if the GPU held that many workgroups; it
     // changes which tiles are split, never the result.  It may only lower the count.
-    long slots = dev->slots;
+    const int n_kv = (Nkv + kBlockN - 1) / kBlockN;
+    // 8-wave workgroups (256-row tiles, one per CU) for long key ranges whose tiles fill
+    // at least one round; 4-wave ones (128 rows, two per CU) otherwise
+    bool wide = D == 128 && n_kv >= 64 && (long)((Nq + 255) / 256) * H * B >= dev->cus;
+    // DTL_ATTN_WAVES (tests, tuning) = 4 or 8 picks the workgroup size for head_dim 128;
+    // like DTL_ATTN_SLOTS it changes the schedule, never the result
+    if (const char* env = getenv("DTL_ATTN_WAVES")) {
+        const long want = strtol(env, nullptr, 10);
+        if (D == 128 && (want == 4 || want == 8)) wide = want == 8;
+    }
+    const int nw = wide ? 8 : 4;
+    long slots = (long)(8 / nw) * dev->cus;
     if (const char* env = getenv("DTL_ATTN_SLOTS")) {
         const long want = strtol(env, nullptr, 10);
         if (want > 0 && want < slots) slots = want;
     }
-    const int n_qtiles = (Nq + kBlockM - 1) / kBlockM;
+    const int n_qtiles = (Nq + 32 * nw - 1) / (32 * nw);
     const long tiles = (long)n_qtiles * H * B;   // the caller has checked that this fits an int
     // Split only where whole tiles would leave most of the GPU idle (streamk.h).  A larger
     // remainder already runs well as whole tiles: with fewer workgroups than slots many
@@ -656,15 +684,15 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // workgroup), while every split piece pays a pipeline start, a publish and a merge, and
     // the split part a second launch; with few key blocks per tile (cross-attention's 512
     // keys) those costs exceed the idle tail.
-    StreamK work = plan_stream_k(tiles, (Nkv + kBlockN - 1) / kBlockN, slots);
+    StreamK work = plan_stream_k(tiles, n_kv, slots);
     // a workspace is needed only when some split range starts inside a tile
     bool split = false;
     for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;
     void* ws = nullptr;
     if (split) {
         static std::atomic<unsigned long long> epochs{0x9E3779B97F4A7C15ull};
-        const size_t acc_bytes = (size_t)work.G_sk * kThreads * (D / 2) * sizeof(float);
-        const size_t ml_bytes = (size_t)work.G_sk * kThreads * 4 * sizeof(float);
+        const size_t acc_bytes = (size_t)work.G_sk * (nw * 64) * (D / 2) * sizeof(float);
+        const size_t ml_bytes = (size_t)work.G_sk * (nw * 64) * 4 * sizeof(float);
         const size_t flag_bytes = (size_t)work.G_sk * sizeof(unsigned long long);
         e = hipMallocFromPoolAsync(&ws, acc_bytes + ml_bytes + flag_bytes, dev->pool, stream);
         if (e != hipSuccess) return e;
@@ -677,19 +705,12 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     auto qq = static_cast<const uint16_t*>(q);
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
-    // whole tiles first (complete rounds of the slots), then the split part
-    if (work.n_dp > 0) {
-        if (D == 128)
-            launch_d<128, false>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
-        else
-            launch_d<64, false>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
-    }
-    if (work.G_sk > 0) {
-        if (D == 128)
-            launch_d<128, true>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
-        else
-            launch_d<64, true>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
-    }
+    if (D == 128 && wide)
+        launch_schedule<128, 8>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
+    else if (D == 128)
+        launch_schedule<128, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
+    else
+        launch_schedule<64, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
     e = hipGetLastError();
     if (ws != nullptr) {
         const hipError_t f = hipFreeAsync(ws, stream);   // stream-ordered: after the kernel

@@ -1,7 +1,7 @@
 // Stream-K work split of the attention kernel (also checked on the host).
 //
-// Tiles are 128-row query tiles ordered (batch, head) major, query tile minor.  With S
-// resident workgroup slots (two per CU), the first floor(tiles / S) * S tiles get one
+// Tiles are query tiles (128 or 256 rows) ordered (batch, head) major, query tile minor.
+// With S resident workgroup slots (two per CU, or one for 256-row tiles), the first floor(tiles / S) * S tiles get one
 // workgroup each (n_dp of them, dispatched in order, XCD-contiguous so that the
 // workgroups of one XCD share a head's K/V in L2).  When the remaining tiles are few (at
 // most S/4) and long (at least 64 key blocks) they would leave most of the GPU idle in a

@@ -18,14 +18,18 @@ __host__ __device__ constexpr int krow_slot(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D>
+// NW: waves of the workgroup that loads the tile (4 or 8); each fills 64 / NW rows.
+template <int D, int NW>
 struct TileLayout {
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static constexpr int kKeys = 64;            // keys per tile
     static constexpr int kRowBytes = 2 * D;     // one key's row
     static constexpr int kChunks = kRowBytes / 16;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows one 1 KB load instruction fills
-    static constexpr int kLoadsPerWave = 16 / kRowsPerLoad; // per tensor: each of 4 waves fills 16 rows
+    static constexpr int kRowsPerWave = kKeys / NW;
+    static constexpr int kLoadsPerWave = kRowsPerWave / kRowsPerLoad;   // per tensor
+    static_assert(kLoadsPerWave >= 1, "a wave fills whole load blocks");
     static constexpr int kTileBytes = kKeys * kRowBytes;
 
     // XOR swizzles of the 16-byte chunk index within a row: chunk c of K row m sits at
@@ -36,10 +40,10 @@ struct TileLayout {
     // Load instruction i of wave w writes the 1 KB block starting at load_block(w, i); its
     // lane l writes bytes [16 l, 16 l + 16) of it: row load_row(w, i, l), position l % kChunks.
     __host__ __device__ static constexpr int load_block(int w, int i) {
-        return (16 * w + kRowsPerLoad * i) * kRowBytes;
+        return (kRowsPerWave * w + kRowsPerLoad * i) * kRowBytes;
     }
     __host__ __device__ static constexpr int load_row(int w, int i, int l) {
-        return 16 * w + kRowsPerLoad * i + l / kChunks;
+        return kRowsPerWave * w + kRowsPerLoad * i + l / kChunks;
     }
     // What that lane loads: the key (within the tile) and the 16-byte chunk of its row.
     __host__ __device__ static constexpr int k_src_key(int w, int i, int l) { return krow_slot(load_row(w, i, l)); }

@@ -5,7 +5,8 @@
 //            sk_owner inverts them; the schedule (plan_stream_k) splits only a short last round
 //   runmap:  for the three permutes and many shapes, RunMap::source agrees with the
 //            element index map written out directly, stays in bounds and is a bijection
-//   tile:    the attention's LDS key-tile layout (head_dim 64 and 128): the direct loads
+//   tile:    the attention's LDS key-tile layout (head_dim 64 and 128, 4- and 8-wave
+//            workgroups): the direct loads
 //            fill every row and chunk of a tile once, the K and V^T fragment reads (the
 //            latter through the transposing read's lane exchange) return exactly the
 //            elements the MFMA operands need, and no read has a bank conflict
@@ -27,18 +28,18 @@ static uint32_t next32() {  // xorshift64*
 }
 
 // A tile in LDS as (key, 16-byte chunk) per 16-byte slot, filled by the load placement.
-template <int D>
+template <int D, int NW>
 static long check_tile_layout() {
-    using L = dtl::TileLayout<D>;
+    using L = dtl::TileLayout<D, NW>;
     long bad = 0;
     auto fail = [&](const char* what, int a, int b, int c) {
-        if (bad < 10) printf("tile D=%d %s %d %d %d\n", D, what, a, b, c);
+        if (bad < 10) printf("tile D=%d NW=%d %s %d %d %d\n", D, NW, what, a, b, c);
         ++bad;
     };
     for (int tensor = 0; tensor < 2; ++tensor) {
         const int slots = L::kTileBytes / 16;
         std::vector<int> key_at(slots, -1), chunk_at(slots, -1), seen(slots, 0);
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < NW; ++w)
             for (int i = 0; i < L::kLoadsPerWave; ++i)
                 for (int l = 0; l < 64; ++l) {
                     const int byte = L::load_block(w, i) + 16 * l;
@@ -223,8 +224,10 @@ int main() {
                     }
                 }
             }
-    bad += check_tile_layout<128>();
-    bad += check_tile_layout<64>();
+    bad += check_tile_layout<128, 4>();
+    bad += check_tile_layout<128, 8>();
+    bad += check_tile_layout<64, 4>();
+    bad += check_tile_layout<64, 8>();
     printf("%s (%ld failures)\n", bad ? "FAIL" : "OK", bad);
     return bad ? 1 : 0;
 }

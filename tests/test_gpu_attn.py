@@ -58,6 +58,29 @@ def test_attention_matches_oracle(shape, o_dtype):
     assert_close("LSE", to_np(lse), l_ref)
 
 
+@pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == 128], ids=lambda s: "B%d_Nq%d_Nkv%d_H%d_D%d_ks%g" % s)
+def test_attention_8_wave_workgroups_match_oracle(shape):
+    """The 256-row-tile kernel (chosen on the GPU for long key ranges) on the same shapes."""
+    import os
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Nkv, H, D, ks = shape
+    log("attn_fwd_lse 8 waves %s" % (shape,))
+    q, k, v = _inputs(1000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
+    old = os.environ.get("DTL_ATTN_WAVES")
+    os.environ["DTL_ATTN_WAVES"] = "8"
+    try:
+        o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=torch.float32)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("DTL_ATTN_WAVES", None)
+        else:
+            os.environ["DTL_ATTN_WAVES"] = old
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("O", to_np(o), o_ref)
+    assert_close("LSE", to_np(lse), l_ref)
+
+
 def test_single_key_output_is_v_bitwise():
     import diffusion_transformer_long_amd as dtl
     for D in (64, 128):

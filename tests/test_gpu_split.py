@@ -6,8 +6,9 @@ GPU held fewer workgroups, which makes small shapes take the same path: whole ti
 the first rounds, the remainder's 64-key blocks spread over the slots, pieces published
 to the workspace and folded in by each tile's finaliser.  The cases cover a tile split
 over 8 workgroups, ranges crossing tile boundaries, the ragged last key block inside a
-split tile, B = 2, D = 64 and 128, bf16 and f32 outputs, and the accumulate entry point
-with rows that hold no keys yet.  Every result is compared with the oracle.
+split tile, B = 2, D = 64 and 128, 4- and 8-wave workgroups (DTL_ATTN_WAVES), bf16 and
+f32 outputs, and the accumulate entry point with rows that hold no keys yet.  Every result
+is compared with the oracle.
 """
 import os
 
@@ -35,6 +36,20 @@ def slots():
         os.environ.pop("DTL_ATTN_SLOTS", None)
     else:
         os.environ["DTL_ATTN_SLOTS"] = old
+
+
+@pytest.fixture
+def waves():
+    """DTL_ATTN_WAVES: the workgroup size (4 or 8 waves) for head_dim 128."""
+    old = os.environ.get("DTL_ATTN_WAVES")
+
+    def set_waves(n):
+        os.environ["DTL_ATTN_WAVES"] = str(n)
+    yield set_waves
+    if old is None:
+        os.environ.pop("DTL_ATTN_WAVES", None)
+    else:
+        os.environ["DTL_ATTN_WAVES"] = old
 
 
 def _inputs(seed, B, Nq, Nkv, H, D, k_scale):
@@ -71,7 +86,34 @@ def test_split_schedule_matches_oracle(slots, case, o_dtype):
     assert_close("LSE", to_np(lse), l_ref)
 
 
-def test_split_schedule_accumulate(slots):
+# 8-wave workgroups (256-row tiles): the same paths with half as many tiles
+CASES8 = [
+    # slots, B, Nq, Nkv, H, D, k_scale      tiles / remainder, key blocks
+    (4, 1, 1152, 4100, 1, 128, 1.0),       # 5 / 1, 65: a 128-row last tile over 4 workgroups
+    (10, 2, 300, 4097, 3, 128, 2.0),       # 12 / 2, 65: ranges cross tiles
+    (4, 1, 129, 64 * 66 + 7, 5, 128, 3.0),  # 5 / 1, 67: 129-row tiles
+    (4, 1, 1024, 4096, 1, 128, 1.0),       # 4 / 0: no split (control)
+]
+
+
+@pytest.mark.parametrize("case", CASES8, ids=lambda c: "slots%d_B%d_Nq%d_Nkv%d_H%d_D%d" % c[:6])
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_split_schedule_8_waves_matches_oracle(slots, waves, case, o_dtype):
+    import diffusion_transformer_long_amd as dtl
+    n, B, Nq, Nkv, H, D, ks = case
+    log("split schedule, 8 waves, slots=%d %s o=%s" % (n, case[1:], o_dtype))
+    q, k, v = _inputs(5000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
+    slots(n)
+    waves(8)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("O", to_np(o), o_ref)
+    assert_close("LSE", to_np(lse), l_ref)
+
+
+@pytest.mark.parametrize("nw", [4, 8])
+def test_split_schedule_accumulate(slots, waves, nw):
     """attn_fwd_lse_accumulate through the split schedule, rows without previous keys."""
     import diffusion_transformer_long_amd as dtl
     B, Nq, Np, Nkv, H, D = 1, 1152, 300, 4100, 1, 128
@@ -89,7 +131,8 @@ def test_split_schedule_accumulate(slots):
     o_c, l_c = oracle.attn(q, k, v)
     o_ref, l_ref = oracle.merge(np.stack([np.nan_to_num(o_p32.astype(np.float64)), o_c]),
                                 np.stack([l_p32.astype(np.float64), l_c]))
-    slots(8)
+    slots(8 if nw == 4 else 4)   # 9 or 5 tiles: one remainder tile split over the slots
+    waves(nw)
     o, lse = dtl.attn_fwd_lse_accumulate(q.to(DEV), k.to(DEV), v.to(DEV),
                                          torch.from_numpy(o_p32).to(DEV), torch.from_numpy(l_p32).to(DEV))
     torch.cuda.synchronize()
