@@ -6,14 +6,17 @@
  *   - Every pointer argument is a DEVICE pointer owned by the caller (for example
  *     the storage of a torch tensor).  The library keeps no pointer after the call
  *     returns.  Only attn_fwd_lse and attn_fwd_lse_accumulate use memory of their own:
- *     on workloads whose last round of tiles they split across the GPU (more 128-row
- *     query tiles than twice the CU count, a remainder of at most a quarter of that,
- *     and at least 4096 keys) they take a workspace of about 35 MB from a memory pool
- *     the library creates per device, stream-ordered on `stream` (allocated before the
- *     kernels, freed after them on the same stream).  The environment variable
- *     DTL_ATTN_SLOTS, when set to a positive number below twice the CU count, makes
- *     that choice as if the GPU held that many workgroups (for tests and tuning; the
- *     result does not change).
+ *     on workloads whose last round of query tiles they split across the GPU (at least
+ *     one full round of tiles over the resident workgroups, a remainder of at most a
+ *     quarter of a round, at least 4096 keys) they take a workspace of about 35 MB from
+ *     a memory pool the library creates per device, stream-ordered on `stream`
+ *     (allocated before the kernels, freed after them on the same stream).  Query tiles
+ *     have 256 rows (one workgroup per CU) for head_dim 128 with at least 4096 keys and
+ *     enough tiles to fill the CUs once, else 128 rows (two workgroups per CU).  For
+ *     tests and tuning, two environment variables change these choices, never the
+ *     result: DTL_ATTN_SLOTS (a positive number below the resident workgroup count)
+ *     schedules as if the GPU held that many workgroups, and DTL_ATTN_WAVES (4 or 8)
+ *     picks 128- or 256-row tiles for head_dim 128.
  *   - Tensors are dense and row-major in the shapes given; there are no strides.
  *     Every pointer must be 16-byte aligned.
  *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.
