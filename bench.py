@@ -279,11 +279,18 @@ def main():
                               reps=20, warmup=3)
         ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts[rot()], lparts[ctr[0]], o=o, lse=lse), reps, warmup=nrot)
 
-        def share_step():
+        def share_step():   # one attn_fwd_lse call per round, then the merge
             dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
-            dtl.attn_fwd_lse_kv_chunks(q, k, v, w3.chunks, parts[0], lparts[0])
-            dtl.attn_merge_lse(parts[0], lparts[0], o=o, lse=lse)
+            dtl.ring_attention(q, k, v, w3.chunks, o_parts=parts[0], lse_parts=lparts[0], o=o, lse=lse)
         ms_step = timer.time(share_step, reps=10, warmup=2)
+
+        def share_step_one():   # the partials of all rounds from one launch, then the merge
+            dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
+            dtl.ring_attention(q, k, v, w3.chunks, o_parts=parts[0], lse_parts=lparts[0], o=o, lse=lse,
+                               one_launch=True)
+        ms_step_one = timer.time(share_step_one, reps=10, warmup=2)
+        ms_chunks_one = timer.time(lambda: dtl.attn_fwd_lse_kv_chunks(q, k, v, w3.chunks, parts[0], lparts[0]),
+                                   reps=20, warmup=3)
         o_acc = parts[1][0]
 
         def share_step_acc():
@@ -300,6 +307,10 @@ def main():
             "step_tflops": round(w3.flops / (ms_step * 1e-3) / 1e12, 2),
             "step_accumulate_ms": round(ms_step_acc, 4),
             "step_accumulate_tflops": round(w3.flops / (ms_step_acc * 1e-3) / 1e12, 2),
+            "step_one_launch_ms": round(ms_step_one, 4),
+            "step_one_launch_tflops": round(w3.flops / (ms_step_one * 1e-3) / 1e12, 2),
+            "all_chunks_one_launch_ms": round(ms_chunks_one, 4),
+            "all_chunks_one_launch_tflops": round(w3.flops / (ms_chunks_one * 1e-3) / 1e12, 2),
             "accumulate_chunk_ms": round(ms_acc, 4),
             "permute_ms": round(ms_perm, 4), "permute_gbs": round(perm_bytes / (ms_perm * 1e-3) / 1e9, 1),
             "permute_bytes": perm_bytes,

@@ -14,10 +14,11 @@ Entry points (same names as the C ABI):
   head_to_seq_permute(y, p, ...)        -> out
   qkv_seq_to_head_permute(x, p, ...)    -> out
   qkv_norm_rope_permute(x, gamma_q, gamma_k, cos, sin, p, ...) -> out
-and two drivers that only sequence those calls:
-  attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  one call per KV chunk
-  ring_attention(q, k, v, chunks)          -> (o, lse)              chunks, then the merge,
-                                                                    or rounds accumulated
+  attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  all KV chunks, one launch
+and a driver that only sequences those calls:
+  ring_attention(q, k, v, chunks)          -> (o, lse)              per-round partials (or
+                                                                    one launch), then the
+                                                                    merge; or rounds accumulated
 """
 from __future__ import annotations
 
@@ -34,8 +35,9 @@ LIB_PATH = os.path.join(_PKG, "libdtl.so")
 DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
 DTL_BF16, DTL_F32 = 0, 1
 
-EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_accumulate", "attn_merge_lse", "seq_to_head_permute", "head_to_seq_permute",
-           "qkv_seq_to_head_permute", "qkv_norm_rope_permute", "dtl_status_string")
+EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_accumulate", "attn_fwd_lse_kv_chunks", "attn_merge_lse",
+           "seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute",
+           "qkv_norm_rope_permute", "dtl_status_string")
 
 
 class DtlError(RuntimeError):
@@ -55,6 +57,8 @@ def _load_library():
     lib.attn_fwd_lse.restype = i
     lib.attn_fwd_lse_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_lse_accumulate.restype = i
+    lib.attn_fwd_lse_kv_chunks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_lse_kv_chunks.restype = i
     lib.attn_merge_lse.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.attn_merge_lse.restype = i
     for name in ("seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute"):
@@ -297,24 +301,32 @@ def attn_fwd_lse_kv_chunks(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ch
                            o_parts: Optional[torch.Tensor] = None,
                            lse_parts: Optional[torch.Tensor] = None,
                            softmax_scale: Optional[float] = None,
+                           o_dtype: torch.dtype = torch.float32,
                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """One attn_fwd_lse call per contiguous KV chunk [t*C, (t+1)*C), as the rounds of Ring
-    attention see them; f32 partials o_parts [P,B,Nq,H,D], lse_parts [P,B,H,Nq].  B must
-    be 1 so that a chunk is a contiguous view of k and v."""
+    """attn_fwd_lse of q against each contiguous KV chunk [t*C, (t+1)*C), C = Nkv/chunks,
+    in one launch: o_parts [P,B,Nq,H,D] (o_dtype, f32 by default), lse_parts [P,B,H,Nq],
+    the layout attn_merge_lse takes."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.bfloat16, 4)
     B, Nq, H, D = q.shape
     Nkv = k.shape[1]
-    if B != 1:
-        raise ValueError("KV chunking by views needs B == 1")
-    if Nkv % chunks != 0:
-        raise ValueError("chunks must divide Nkv")
-    C = Nkv // chunks
+    if tuple(k.shape) != (B, Nkv, H, D) or tuple(v.shape) != (B, Nkv, H, D):
+        raise ValueError("k and v must be [B, Nkv, H, D] matching q %s" % (tuple(q.shape),))
+    if chunks <= 0 or Nkv % chunks != 0:
+        raise ValueError("chunks must be positive and divide Nkv")
+    P = chunks
     if o_parts is None:
-        o_parts = torch.empty((chunks, B, Nq, H, D), dtype=torch.float32, device=q.device)
+        o_parts = torch.empty((P, B, Nq, H, D), dtype=o_dtype, device=q.device)
     if lse_parts is None:
-        lse_parts = torch.empty((chunks, B, H, Nq), dtype=torch.float32, device=q.device)
-    for t in range(chunks):
-        attn_fwd_lse(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C], o=o_parts[t],
-                     lse=lse_parts[t], softmax_scale=softmax_scale, stream=stream)
+        lse_parts = torch.empty((P, B, H, Nq), dtype=torch.float32, device=q.device)
+    _dev(o_parts, "o_parts", None, 5)
+    _dev(lse_parts, "lse_parts", torch.float32, 4)
+    if tuple(o_parts.shape) != (P, B, Nq, H, D) or tuple(lse_parts.shape) != (P, B, H, Nq):
+        raise ValueError("o_parts must be [P,B,Nq,H,D] and lse_parts [P,B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_lse_kv_chunks(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
+                                      lse_parts.data_ptr(), B, Nq, Nkv, H, D, P, scale,
+                                      _dtype_code(o_parts.dtype), _stream(q, stream)))
     return o_parts, lse_parts
 
 
@@ -323,26 +335,40 @@ def ring_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: in
                    o_parts: Optional[torch.Tensor] = None, lse_parts: Optional[torch.Tensor] = None,
                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    accumulate: bool = False, o_acc: Optional[torch.Tensor] = None,
+                   one_launch: bool = False,
                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention over all keys computed as Ring attention's rounds on one GPU, over
-    contiguous KV chunks [t*C, (t+1)*C) (B must be 1).
+    contiguous KV chunks [t*C, (t+1)*C) (B must be 1 for the per-round forms, whose
+    chunks are views of k and v).
 
-    accumulate=False: per-chunk f32 partials (o_parts, lse_parts), then the LSE merge.
+    accumulate=False: one attn_fwd_lse call per round into f32 partials (o_parts,
+    lse_parts), then the LSE merge; with one_launch=True the partials of all rounds come
+    from one attn_fwd_lse_kv_chunks call (any B).
     accumulate=True: the first round writes an f32 running result (o_acc, and lse), each
     later round folds its chunk into it with attn_fwd_lse_accumulate, and the last round
     writes the final o in out_dtype; no partials are stored."""
-    if not accumulate:
-        o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
-                                                    softmax_scale, stream)
-        return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype,
-                              stream=stream)
     B, Nq, H, D = q.shape
     Nkv = k.shape[1]
+    if chunks <= 0 or Nkv % chunks != 0:
+        raise ValueError("chunks must be positive and divide Nkv")
+    if not accumulate and one_launch:
+        o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
+                                                    softmax_scale, stream=stream)
+        return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype,
+                              stream=stream)
     if B != 1:
         raise ValueError("KV chunking by views needs B == 1")
-    if Nkv % chunks != 0:
-        raise ValueError("chunks must divide Nkv")
     C = Nkv // chunks
+    if not accumulate:
+        if o_parts is None:
+            o_parts = torch.empty((chunks, B, Nq, H, D), dtype=torch.float32, device=q.device)
+        if lse_parts is None:
+            lse_parts = torch.empty((chunks, B, H, Nq), dtype=torch.float32, device=q.device)
+        for t in range(chunks):
+            attn_fwd_lse(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C], o=o_parts[t],
+                         lse=lse_parts[t], softmax_scale=softmax_scale, stream=stream)
+        return attn_merge_lse(o_parts, lse_parts, o=o, lse=lse, out_dtype=out_dtype,
+                              stream=stream)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if chunks == 1:

@@ -158,8 +158,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, void* o, float* lse,
                      const float* o_prev, const float* lse_prev,
-                     int Nq, int Nkv, int H, float scale_log2, int n_qtiles, int tile_base,
-                     StreamK work) {
+                     int Nq, int Nkv, int H, int q_batches, int kv_chunks, float scale_log2,
+                     int n_qtiles, int tile_base, StreamK work) {
     constexpr int kThreads = NW * 64;
     constexpr int kBlockM = NW * 32;   // query rows per workgroup
     using L = TileLayout<D, NW>;
@@ -380,11 +380,13 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const int qt = tile % n_qtiles;
         const int bh = tile / n_qtiles;
         h = bh % H;
-        b = bh / H;
-        kbase = k + ((long)b * Nkv * H + h) * D;
-        vbase = v + ((long)b * Nkv * H + h) * D;
+        b = bh / H;                              // output batch: chunk-major (t * q_batches + bq)
+        const int bq = b % q_batches;            // the query batch
+        const long bkv = (long)bq * kv_chunks + b / q_batches;   // its key chunk, Nkv keys long
+        kbase = k + (bkv * Nkv * H + h) * D;
+        vbase = v + (bkv * Nkv * H + h) * D;
         qrow = qt * kBlockM + wave * 32 + r;
-        const uint16_t* qp = q + (((long)b * Nq + qrow) * H + h) * D + 8 * g;
+        const uint16_t* qp = q + (((long)bq * Nq + qrow) * H + h) * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             u32x4 x = qrow < Nq ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
@@ -580,25 +582,25 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 template <int D, int NW, bool OUT_F32, bool ACCUM, bool SPLIT>
 void launch_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
-                const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
-                float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
-                hipStream_t stream) {
+                const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
+                int kvc, float scale_log2, int n_qtiles, int grid, int tile_base,
+                const StreamK& work, hipStream_t stream) {
     attn_fwd_kernel<D, NW, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
-        q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, tile_base, work);
+        q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, tile_base, work);
 }
 
 template <int D, int NW, bool SPLIT>
 void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
-              const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
-              float scale_log2, int n_qtiles, int grid, int tile_base, const StreamK& work,
-              bool out_f32, hipStream_t stream) {
+              const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
+              int kvc, float scale_log2, int n_qtiles, int grid, int tile_base,
+              const StreamK& work, bool out_f32, hipStream_t stream) {
     const bool accum = o_prev != nullptr;
     if (out_f32) {
-        if (accum) launch_one<D, NW, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, NW, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
     } else {
-        if (accum) launch_one<D, NW, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, NW, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
     }
 }
 
@@ -606,13 +608,13 @@ void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, 
 // split part
 template <int D, int NW>
 void launch_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
-                     const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H,
-                     float scale_log2, int n_qtiles, const StreamK& work, bool out_f32,
+                     const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
+                     int kvc, float scale_log2, int n_qtiles, const StreamK& work, bool out_f32,
                      hipStream_t stream) {
     if (work.n_dp > 0)
-        launch_d<D, NW, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
+        launch_d<D, NW, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.n_dp, 0, work, out_f32, stream);
     if (work.G_sk > 0)
-        launch_d<D, NW, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+        launch_d<D, NW, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
 }
 
 // Per-device launch facts: compute units and a memory pool for the stream-ordered
@@ -654,7 +656,12 @@ hipError_t device_info(DeviceInfo** out) {
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
-                           int H, int D, float scale, bool out_f32, hipStream_t stream) {
+                           int H, int D, int P, float scale, bool out_f32, hipStream_t stream) {
+    // P > 1: P equal key chunks of Nkv / P keys each, one result per (chunk, batch), as
+    // if the chunks were P * B batches sharing the batch's queries
+    const int Bq = B;
+    B *= P;
+    Nkv /= P;
     DeviceInfo* dev = nullptr;
     hipError_t e = device_info(&dev);
     if (e != hipSuccess) return e;
@@ -706,11 +713,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
     if (D == 128 && wide)
-        launch_schedule<128, 8>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<128, 8>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     else if (D == 128)
-        launch_schedule<128, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<128, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     else
-        launch_schedule<64, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<64, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     e = hipGetLastError();
     if (ws != nullptr) {
         const hipError_t f = hipFreeAsync(ws, stream);   // stream-ordered: after the kernel

@@ -37,15 +37,16 @@ const char* dtl_status_string(dtl_status s) {
 
 namespace {
 
-// Shared validation and launch of attn_fwd_lse and attn_fwd_lse_accumulate (o_prev ==
-// nullptr for the former).
+// Shared validation and launch of attn_fwd_lse, attn_fwd_lse_accumulate (o_prev set) and
+// attn_fwd_lse_kv_chunks (P > 1 chunks: o and lse hold P results).
 dtl_status attn_call(const void* q, const void* k, const void* v, const float* o_prev,
                      const float* lse_prev, void* o, float* lse, int B, int Nq, int Nkv, int H,
-                     int D, float softmax_scale, dtl_dtype o_dtype, bool accum,
+                     int D, int P, float softmax_scale, dtl_dtype o_dtype, bool accum,
                      hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return DTL_ERR_INVALID_ARG;
     if (accum && (!o_prev || !lse_prev)) return DTL_ERR_INVALID_ARG;
     if (B <= 0 || Nq <= 0 || Nkv <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
+    if (P <= 0 || Nkv % P != 0 || (accum && P != 1)) return DTL_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DTL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return DTL_ERR_INVALID_ARG;
@@ -54,8 +55,8 @@ dtl_status attn_call(const void* q, const void* k, const void* v, const float* o
     if (o_dtype != DTL_BF16 && o_dtype != DTL_F32) return DTL_ERR_UNSUPPORTED;
     const long q_bytes = (long)B * Nq * H * D * 2;
     const long kv_bytes = (long)B * Nkv * H * D * 2;
-    const long o_bytes = (long)B * Nq * H * D * (o_dtype == DTL_F32 ? 4 : 2);
-    const long l_bytes = (long)B * H * Nq * 4;
+    const long o_bytes = (long)P * B * Nq * H * D * (o_dtype == DTL_F32 ? 4 : 2);
+    const long l_bytes = (long)P * B * H * Nq * 4;
     if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
         overlap(o, o_bytes, v, kv_bytes) || overlap(o, o_bytes, lse, l_bytes) ||
         overlap(lse, l_bytes, q, q_bytes) || overlap(lse, l_bytes, k, kv_bytes) ||
@@ -71,12 +72,12 @@ dtl_status attn_call(const void* q, const void* k, const void* v, const float* o
             overlap(o, o_bytes, lse_prev, l_bytes) || overlap(lse, l_bytes, o_prev, op_bytes))
             return DTL_ERR_INVALID_ARG;
     }
-    const long tiles = ((long)Nq + 127) / 128 * H * B;
-    if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)B * Nq * H > kIntMax ||
+    const long tiles = ((long)Nq + 127) / 128 * H * B * P;
+    if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)P * B * Nq * H > kIntMax ||
         (long)H * D > (1l << 24))
         return DTL_ERR_INVALID_ARG;
     hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, accum ? o_prev : nullptr,
-                                        accum ? lse_prev : nullptr, B, Nq, Nkv, H, D,
+                                        accum ? lse_prev : nullptr, B, Nq, Nkv, H, D, P,
                                         softmax_scale, o_dtype == DTL_F32, stream);
     return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
 }
@@ -88,15 +89,22 @@ extern "C" {
 dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Nq, int Nkv, int H, int D, float softmax_scale,
                         dtl_dtype o_dtype, hipStream_t stream) {
-    return attn_call(q, k, v, nullptr, nullptr, o, lse, B, Nq, Nkv, H, D, softmax_scale,
+    return attn_call(q, k, v, nullptr, nullptr, o, lse, B, Nq, Nkv, H, D, 1, softmax_scale,
                      o_dtype, false, stream);
+}
+
+dtl_status attn_fwd_lse_kv_chunks(const void* q, const void* k, const void* v, void* o_parts,
+                                  float* lse_parts, int B, int Nq, int Nkv, int H, int D, int P,
+                                  float softmax_scale, dtl_dtype o_dtype, hipStream_t stream) {
+    return attn_call(q, k, v, nullptr, nullptr, o_parts, lse_parts, B, Nq, Nkv, H, D, P,
+                     softmax_scale, o_dtype, false, stream);
 }
 
 dtl_status attn_fwd_lse_accumulate(const void* q, const void* k, const void* v,
                                    const float* o_prev, const float* lse_prev, void* o,
                                    float* lse, int B, int Nq, int Nkv, int H, int D,
                                    float softmax_scale, dtl_dtype o_dtype, hipStream_t stream) {
-    return attn_call(q, k, v, o_prev, lse_prev, o, lse, B, Nq, Nkv, H, D, softmax_scale,
+    return attn_call(q, k, v, o_prev, lse_prev, o, lse, B, Nq, Nkv, H, D, 1, softmax_scale,
                      o_dtype, true, stream);
 }
 

@@ -119,6 +119,29 @@ dtl_status attn_fwd_lse_accumulate(const void *q, const void *k, const void *v,
                                    float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_lse_kv_chunks - attn_fwd_lse over P equal, contiguous key chunks in one call:
+ * the partial results that Ring attention's P rounds produce on one rank (the KV blocks
+ * [t*C, (t+1)*C), C = Nkv / P, that the ring delivers in turn: arganzheng.life,
+ * multi-GPU diffusion parallelism, section 4.2 "Ring"; MindIE SD "多卡并行" page, Ring
+ * Sequence Parallel section), laid out as attn_merge_lse takes them.  For each chunk t,
+ * (o_parts[t], lse_parts[t]) is what attn_fwd_lse returns for q against keys and
+ * values [t*C, (t+1)*C); merging the P results gives attention over all Nkv keys.  One
+ * call keeps every (chunk, query tile) pair on the GPU at once, where P separate calls
+ * on short chunks would each leave CUs idle.
+ *
+ *   q, k, v, softmax_scale   as attn_fwd_lse (k and v hold all Nkv keys)
+ *   o_parts    o_dtype [P, B, Nq, H, D]
+ *   lse_parts  f32 [P, B, H, Nq]
+ *   P          number of chunks, >= 1, dividing Nkv
+ *
+ * Errors: as attn_fwd_lse, and DTL_ERR_INVALID_ARG for P <= 0 or P not dividing Nkv.
+ */
+dtl_status attn_fwd_lse_kv_chunks(const void *q, const void *k, const void *v,
+                                  void *o_parts, float *lse_parts,
+                                  int B, int Nq, int Nkv, int H, int D, int P,
+                                  float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
+
+/*
  * attn_merge_lse - exact merge of P partial attention results over disjoint key sets.
  *
  * For every (b, n, h), with parts t = 0..P-1:

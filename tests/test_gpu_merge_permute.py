@@ -106,6 +106,53 @@ def test_ring_equivalence_on_gpu_partials():
         assert_close("ring %d chunks LSE" % chunks, to_np(lse), l_ref)
 
 
+KV_CHUNK_CASES = [
+    # B, Nq, Nkv, H, D, P, waves (None: the library's choice)
+    (2, 63, 4 * 65, 3, 128, 4, None),     # ragged 65-key chunks, B = 2
+    (1, 200, 3 * 129, 2, 64, 3, None),
+    (1, 130, 2 * 1000, 2, 128, 2, None),
+    (2, 300, 5 * 77, 1, 64, 5, None),
+    (1, 97, 300, 2, 128, 1, None),         # P = 1 is attn_fwd_lse
+    (2, 63, 4 * 65, 3, 128, 4, 8),        # 256-row tiles
+    (1, 257, 2 * 4160, 1, 128, 2, 8),
+]
+
+
+@pytest.mark.parametrize("case", KV_CHUNK_CASES, ids=lambda c: "B%d_Nq%d_Nkv%d_H%d_D%d_P%d_w%s" % c)
+def test_kv_chunks_one_launch_match_oracle(case):
+    """attn_fwd_lse_kv_chunks: part t is attention over keys [tC, (t+1)C), and the merge of
+    the parts is attention over all keys (also through ring_attention(one_launch=True))."""
+    import os
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Nkv, H, D, P, nw = case
+    log("attn_fwd_lse_kv_chunks %s" % (case,))
+    g = np.random.Generator(np.random.PCG64(7000 + Nq + Nkv + P))
+    q = synthetic.to_bf16(g.standard_normal((B, Nq, H, D), dtype=np.float32))
+    k = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32) * 2)
+    v = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    old = os.environ.get("DTL_ATTN_WAVES")
+    if nw is not None:
+        os.environ["DTL_ATTN_WAVES"] = str(nw)
+    try:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        o_parts, l_parts = dtl.attn_fwd_lse_kv_chunks(qd, kd, vd, P)
+        o, lse = dtl.ring_attention(qd, kd, vd, P, one_launch=True, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("DTL_ATTN_WAVES", None)
+        else:
+            os.environ["DTL_ATTN_WAVES"] = old
+    C = Nkv // P
+    for t in range(P):
+        o_ref, l_ref = oracle.attn(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C])
+        assert_close("part %d O" % t, to_np(o_parts[t]), o_ref)
+        assert_close("part %d LSE" % t, to_np(l_parts[t]), l_ref)
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("merged O", to_np(o), o_ref)
+    assert_close("merged LSE", to_np(lse), l_ref)
+
+
 # ------------------------------------------------------------------ permute
 
 @pytest.mark.parametrize("p,B,N,H,D,dtype", [

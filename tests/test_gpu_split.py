@@ -140,6 +140,20 @@ def test_split_schedule_accumulate(slots, waves, nw):
     assert_close("LSE", to_np(lse), l_ref)
 
 
+def test_split_schedule_kv_chunks(slots):
+    """attn_fwd_lse_kv_chunks through the split schedule: 2 chunks of 4100 keys, 18 tiles
+    on 8 slots (a remainder of 2 tiles split), each part against the oracle."""
+    import diffusion_transformer_long_amd as dtl
+    q, k, v = _inputs(92, 1, 1152, 2 * 4100, 1, 128, 2.0)
+    slots(8)
+    o_parts, l_parts = dtl.attn_fwd_lse_kv_chunks(q.to(DEV), k.to(DEV), v.to(DEV), 2)
+    torch.cuda.synchronize()
+    for t in range(2):
+        o_ref, l_ref = oracle.attn(q, k[:, t * 4100:(t + 1) * 4100], v[:, t * 4100:(t + 1) * 4100])
+        assert_close("part %d O" % t, to_np(o_parts[t]), o_ref)
+        assert_close("part %d LSE" % t, to_np(l_parts[t]), l_ref)
+
+
 def test_split_schedule_repeated_calls_agree(slots):
     """Back-to-back split launches (fresh epochs, reused pool memory) give one result."""
     import diffusion_transformer_long_amd as dtl

@@ -69,6 +69,22 @@ def test_attn_fwd_lse_validation():
     assert _attn(lib, dt=7) == UNS
 
 
+def test_attn_fwd_lse_kv_chunks_validation():
+    import diffusion_transformer_long_amd as dtl
+    lib = dtl.lib
+    INV, UNS = dtl.DTL_ERR_INVALID_ARG, dtl.DTL_ERR_UNSUPPORTED
+
+    def call(q=A, k=Bp, v=C, o=Dp, lse=E, B=1, Nq=128, Nkv=256, H=2, D=128, P=2, scale=0.088, dt=1):
+        return lib.attn_fwd_lse_kv_chunks(q, k, v, o, lse, B, Nq, Nkv, H, D, P, scale, dt, None)
+    for P in (0, -1, 3):                      # P must be positive and divide Nkv
+        assert call(P=P) == INV, P
+    assert call(o=None) == INV
+    assert call(Nkv=0) == INV
+    assert call(o=A + 64) == INV              # parts overlap q
+    assert call(lse=Dp + 128 * 2 * 128 * 4) == INV   # lse inside the second part of o
+    assert call(D=96) == UNS
+
+
 def test_attn_fwd_lse_accumulate_validation():
     import diffusion_transformer_long_amd as dtl
     lib = dtl.lib
