@@ -41,6 +41,8 @@ SHAPES = [
     (2, 300, 77, 1, 64, 1.0),
     (1, 257, 513, 4, 64, 2.0),
     (1, 384, 2049, 2, 128, 1.0),
+    (2, 130, 200, 6, 128, 2.0),     # short last tiles of 8 of the 12 (batch, head) pairs go first
+    (1, 257, 513, 16, 64, 1.0),     # 16 short last tiles first
 ]
 
 
