@@ -168,6 +168,10 @@ def test_binding_rejects_cpu_tensors_and_bad_shapes():
     with pytest.raises(ValueError):
         dtl.attn_fwd_lse(x, x, x)
     with pytest.raises(ValueError):
+        dtl.attn_fwd_lse_kv_chunks(x, x, x, 2)
+    with pytest.raises(ValueError):
+        dtl.ring_attention(x, x, x, 3)   # 3 does not divide the 8 keys
+    with pytest.raises(ValueError):
         dtl.seq_to_head_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
     with pytest.raises(ValueError):
         dtl.head_to_seq_permute(torch.zeros((2, 1, 4, 2, 8)), 2)
