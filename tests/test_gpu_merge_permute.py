@@ -118,6 +118,25 @@ KV_CHUNK_CASES = [
 ]
 
 
+def test_kv_chunks_bf16_parts():
+    """attn_fwd_lse_kv_chunks with bf16 partials: each part is attn_fwd_lse's bf16 result."""
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Nkv, H, D, P = 1, 150, 3 * 100, 4, 128, 3
+    g = np.random.Generator(np.random.PCG64(7777))
+    q = synthetic.to_bf16(g.standard_normal((B, Nq, H, D), dtype=np.float32))
+    k = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32) * 3)
+    v = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_parts, l_parts = dtl.attn_fwd_lse_kv_chunks(qd, kd, vd, P, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o_parts.dtype == torch.bfloat16
+    C = Nkv // P
+    for t in range(P):
+        o_ref, l_ref = oracle.attn(q, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C])
+        assert_close("part %d O" % t, to_np(o_parts[t]), o_ref)
+        assert_close("part %d LSE" % t, to_np(l_parts[t]), l_ref)
+
+
 @pytest.mark.parametrize("case", KV_CHUNK_CASES, ids=lambda c: "B%d_Nq%d_Nkv%d_H%d_D%d_P%d_w%s" % c)
 def test_kv_chunks_one_launch_match_oracle(case):
     """attn_fwd_lse_kv_chunks: part t is attention over keys [tC, (t+1)C), and the merge of
