@@ -1,9 +1,9 @@
 // Stream-K work split of the attention kernel (also checked on the host).
 //
 // Tiles are query tiles (128 or 256 rows) ordered (batch, head) major, query tile minor.
-// With S resident workgroup slots (two per CU, or one for 256-row tiles), the first floor(tiles / S) * S tiles get one
-// workgroup each (n_dp of them, dispatched in order, XCD-contiguous so that the
-// workgroups of one XCD share a head's K/V in L2).  When the remaining tiles are few (at
+// With S resident workgroup slots (two per CU, or one for 256-row tiles), the first
+// floor(tiles / S) * S tiles (n_dp of them) are taken whole by S persistent workgroups,
+// in XCD-contiguous order so that the workgroups of one XCD share a head's K/V in L2.  When the remaining tiles are few (at
 // most S/4) and long (at least 64 key blocks) they would leave most of the GPU idle in a
 // last round for a long time, so their work is split evenly over G_sk workgroups of a
 // second launch ("stream-K", plan_stream_k): W units, a unit being one 64-key block of one
@@ -40,6 +40,7 @@ struct StreamK {
     float* ws_ml;               // [G_sk][threads][4] reference max, row-sum half, 2 unused
     unsigned long long* flag;   // [G_sk]
     unsigned long long epoch;   // this launch's flag value
+    int slots;                  // resident workgroups the schedule assumes (whole-tile grid bound)
 };
 
 // First unit of split-part workgroup g (g = G_sk gives W).
