@@ -69,6 +69,9 @@ def parse():
                     help="comma list of extra legs (or 'none'); 'copy' adds a plain copy kernel "
                          "used to calibrate HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline workload (for profiling one leg at a time); the JSON "
+                         "line then carries the legs only, with value null")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--print-source-hash", action="store_true",
@@ -180,41 +183,43 @@ def main():
 
     # ---------------------------------------------------------------- headline
     w = synthetic.FLUX
-    err("[bench] headline %s: generating inputs" % w.name)
-    q, k, v = (t.to(dev) for t in synthetic.workload_qkv(w))
-    o = torch.empty((w.B, w.Nq, w.H, w.D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    value = ms_per_step = roofline = None
+    if not args.no_headline:
+        err("[bench] headline %s: generating inputs" % w.name)
+        q, k, v = (t.to(dev) for t in synthetic.workload_qkv(w))
+        o = torch.empty((w.B, w.Nq, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
 
-    def step():
-        dtl.attn_fwd_lse(q, k, v, o=o, lse=lse)
+        def step():
+            dtl.attn_fwd_lse(q, k, v, o=o, lse=lse)
 
-    prewarm(torch, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
-    err("[bench] headline: %.3f ms/step (wall), %.3f ms/launch (events), %.1f TFLOP/s"
-        % (ms_per_step, kernel_ms, achieved))
+        prewarm(torch, dev)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
+        kernel_ms = ev0.elapsed_time(ev1) / args.steps
+        value = w.flops / (ms_per_step * 1e-3) / 1e12
+        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        err("[bench] headline: %.3f ms/step (wall), %.3f ms/launch (events), %.1f TFLOP/s"
+            % (ms_per_step, kernel_ms, achieved))
 
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": pmc_traffic(),
-                "kernel": "attn_fwd_kernel<128,bf16> on %s" % w.name,
-                "flops_per_launch": w.flops,
-                "algorithmic_bytes_per_launch": 2 * (3 + 1) * w.B * w.Nq * w.H * w.D + 4 * w.B * w.H * w.Nq}
-    del q, k, v, o, lse
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": pmc_traffic(),
+                    "kernel": "attn_fwd_kernel<128,bf16> on %s" % w.name,
+                    "flops_per_launch": w.flops,
+                    "algorithmic_bytes_per_launch": 2 * (3 + 1) * w.B * w.Nq * w.H * w.D + 4 * w.B * w.H * w.Nq}
+        del q, k, v, o, lse
 
     legs = {}
 
@@ -398,20 +403,21 @@ def main():
         del a, b
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.no_headline:
         err("[bench] cpu baseline (oracle on host cores)")
         cpu = cpu_baseline(w, args.cpu_seconds)
         err("[bench] cpu baseline: %s" % cpu)
 
     line = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=4608 and N=27280, 1 GPU",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "value": None if value is None else round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None if ms_per_step is None else round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "seq_len": w.Nq, "heads": w.H, "head_dim": w.D,
                    "k_scale": w.k_scale, "causal": False, "o_dtype": "bf16", "lse_dtype": "f32",
                    "parallelism": "none (one GPU's full sequence)"},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "frac_of_peak": None if value is None else round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": legs,
