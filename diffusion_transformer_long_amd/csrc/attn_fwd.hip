@@ -29,10 +29,11 @@
 //   per-lane scalar.
 //
 // Softmax in base 2: p = exp2(s * scale*log2(e) - m), m a reference max of the scaled
-// logits in log2 units, updated once per 32-key half.  The reference is only moved when
-// some row's half-tile max exceeds it by more than kRescaleThreshold (the accumulators
-// are then rescaled); otherwise p <= 2^threshold, which f32 and bf16 hold without
-// overflow.  The row sum is taken over the bf16-rounded weights (two per v_dot2 against
+// logits in log2 units.  A 32-key half's weights are first taken against the current
+// reference; only when some lane's sum of its 16 weights exceeds 2^kRescaleThreshold (or is
+// +inf or NaN, as in a row's first half) is the reference moved to a little above the half's
+// row max, the accumulators rescaled and the weights taken again.  So p <= 2^threshold always, which
+// f32 and bf16 hold without overflow, and the row max is formed only on that rare path.  The row sum is taken over the bf16-rounded weights (two per v_dot2 against
 // (1, 1)), i.e. over exactly the weights the P.V product uses.  The result is the same
 // softmax, since numerator and denominator share the reference m.
 //
@@ -66,7 +67,8 @@ namespace {
 // (measured 5.5% faster at FLUX N=4608, 1.6% at Wan2.2-5B, 2% at the Wan2.1-14B chunk, but
 // slower at 512 keys and at 1152 x 1152 Ring chunks, which keep NW = 4).
 constexpr int kBlockN = 64;            // keys per iteration
-// The running max moves only when a tile half raises it by more than this (log2 units).
+// Weights are kept at most 2^this: the running max moves only when a tile half's weights
+// against it would exceed that (log2 units; tested on each lane's sum of its weights).
 // A larger threshold skips more accumulator rescales; the dominant weight of a peaked row
 // is then exp2(x) with x in (0, threshold] instead of exactly 1, whose bf16 rounding the
 // rounded-weight row sum below cancels (with an f32 row sum a threshold of 8 would triple
@@ -76,6 +78,16 @@ constexpr int kBlockN = 64;            // keys per iteration
 #define DTL_RESCALE_THRESHOLD 8.0f
 #endif
 constexpr float kRescaleThreshold = DTL_RESCALE_THRESHOLD;
+static_assert(kRescaleThreshold == (float)(int)kRescaleThreshold && kRescaleThreshold >= 0.0f,
+              "a whole number of doublings");
+constexpr float pow2_int(int n) { return n == 0 ? 1.0f : 2.0f * pow2_int(n - 1); }
+// the same bound on a lane's sum of 16 weights (2^kRescaleThreshold)
+constexpr float kMaxLaneSum = pow2_int((int)kRescaleThreshold);
+// When the reference moves, it goes this far (log2 units) above the half's row max: the
+// weights are floating point, so scaling them all by 2^-4 costs no precision, and later
+// keys must then exceed that max by more (about 8 to 12 units instead of 4 to 8) before the
+// reference moves again (peaked FLUX-like rows: 6% faster on 1152-key Ring chunks).
+constexpr float kHeadroom = 4.0f;
 // A tile's finaliser polls its helpers' flags at most this often (s_sleep 8 between
 // polls, ~0.2 us; the bound is ~4 ms), then computes the missing keys itself.
 constexpr int kMaxPolls = 20000;
@@ -226,21 +238,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     using FULL = std::false_type;
     using PARTIAL = std::true_type;
 
-    // Online-softmax update for one 32-key half of a tile: moves the reference max when the
-    // half raises it by more than kRescaleThreshold, then rounds exp2(s*c - m) to bf16 for the
-    // P.V product and returns the f32 sum of this lane's 16 rounded weights.  Returns whether the
-    // accumulators need the rescale by alpha (wave-uniform).
-    auto softmax_half = [&](const f32x16& s, bf16x8 (&pf)[2], float& lsum, float& alpha) -> bool {
-        float mx = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        const float mx2 = halves_max(mx) * scale_log2;
-        const bool rescale = __any(mx2 > m_run + kRescaleThreshold);
-        const float m_new = rescale ? fmaxf(m_run, mx2) : m_run;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 when unchanged
-        m_run = m_new;
-        l_run *= alpha;
-        lsum = 0.f;
+    // Weights of one 32-key half against the current reference max m_run: exp2(s*c - m_run)
+    // rounded to bf16 for the P.V product; returns the f32 sum of this lane's 16 rounded
+    // weights.  The row sum is taken over the rounded weights, two per v_dot2 against (1, 1):
+    // numerator (P.V on the bf16 P) and denominator then round the same way.
+    auto half_weights = [&](const f32x16& s, bf16x8 (&pf)[2]) -> float {
+        float lsum = 0.f;
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -249,14 +252,37 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             for (int i = 0; i < 8; ++i)
                 e[i] = __builtin_amdgcn_exp2f(fmaf(s[hf * 8 + i], scale_log2, -m_run));
             pf[hf] = __builtin_convertvector(e, bf16x8);
-            // the row sum is taken over the rounded weights, two per v_dot2 against (1, 1):
-            // numerator (P.V on the bf16 P) and denominator then round the same way
             lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 0, 1), ones, lsum, false);
             lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 2, 3), ones, lsum, false);
             lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 4, 5), ones, lsum, false);
             lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[hf], pf[hf], 6, 7), ones, lsum, false);
         }
-        return rescale;
+        return lsum;
+    };
+
+    // Online-softmax update for one 32-key half of a tile.  The weights are first taken
+    // against the current reference max.  They are non-negative, so when every lane's sum of
+    // its 16 weights is at most 2^kRescaleThreshold, so is every weight: the reference stays
+    // and no row max is formed (the common case once a row's larger logits have been seen).
+    // Otherwise (a larger weight, or the +inf / NaN weights of a row's first half, whose
+    // reference is still -inf) the reference moves to kHeadroom above the half's row max, the
+    // accumulators need the rescale by alpha, and the weights are taken again.  Returns whether the rescale
+    // is needed (wave-uniform); lsum is the f32 sum of this lane's 16 rounded weights.
+    auto softmax_half = [&](const f32x16& s, bf16x8 (&pf)[2], float& lsum, float& alpha) -> bool {
+        lsum = half_weights(s, pf);
+        alpha = 1.0f;
+        // compared as bit patterns: a non-negative float orders like its bits, and +inf and
+        // the NaNs lie above every finite bound (the kernel is built without NaN semantics)
+        if (__all(__float_as_uint(lsum) <= __float_as_uint(kMaxLaneSum))) return false;
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        const float m_new = fmaxf(m_run, halves_max(mx) * scale_log2 + kHeadroom);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 from a -inf reference, 1 if unchanged
+        m_run = m_new;
+        l_run *= alpha;
+        lsum = half_weights(s, pf);
+        return true;
     };
     auto rescale_acc = [&](float alpha) {
 #pragma unroll
