@@ -20,8 +20,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
-# The attention kernel's values are finite or -inf (masked keys, empty rows) and it never
-# reads an operand that could hold a NaN, so its max needs no NaN quieting of operands.
+# The attention kernel's row max runs over logits that are finite or -inf (masked keys), so
+# it needs no NaN quieting of operands.  A row's first weights, taken against a -inf reference,
+# can be +inf or NaN; the kernel tests their sum as a bit pattern, which this flag cannot fold.
 EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"]}
 
 
