@@ -124,6 +124,27 @@ def test_explicit_scale():
     assert_close("LSE scale 0.05", to_np(lse), l_ref)
 
 
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_logit_ramp_along_keys(order):
+    """Keys scaled by a ramp along the key axis (logit std 0.25 -> 4, or the reverse). Ascending,
+    every later tile holds larger logits than all before it, so the running reference moves and
+    the accumulators are rescaled again and again; descending, the largest logits come first and
+    the reference stays put after the first tiles."""
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Nkv, H, D = 1, 130, 700, 3, 128
+    q, k, v = _inputs(101 if order == "ascending" else 103, B, Nq, Nkv, H, D)
+    ramp = np.linspace(0.25, 4.0, Nkv, dtype=np.float32)
+    if order == "descending":
+        ramp = ramp[::-1].copy()
+    k = synthetic.to_bf16(k.float().numpy() * ramp[None, :, None, None])
+    log("attn_fwd_lse logit ramp %s" % order)
+    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("O ramp " + order, to_np(o), o_ref)
+    assert_close("LSE ramp " + order, to_np(lse), l_ref)
+
+
 def test_deterministic_and_no_writes_past_outputs():
     import diffusion_transformer_long_amd as dtl
     B, Nq, Nkv, H, D = 1, 333, 517, 3, 128
