@@ -319,12 +319,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     //   P.V of half 1
     // Meanwhile the next tile (PF: 0 none, 1 a full tile, 2 the ragged last tile) travels
     // into the other buffer; the wait for it sits right before the closing barrier.
-    // buf_c is the LDS buffer of tile `it` (it & 1): a std::integral_constant in the steady
-    // loop, so that every LDS address is a lane offset plus an immediate, or an int elsewhere.
-    auto step = [&](auto pf_c, auto mask_c, int it, auto buf_c) {
+    auto step = [&](auto pf_c, auto mask_c, int it) {
         constexpr int PF = decltype(pf_c)::value;
         constexpr bool MASK = decltype(mask_c)::value;
-        const int buf = buf_c;
+        const int buf = it & 1;
         const int kv0 = it * kBlockN;
 
         const LDS_AS char* sk = (const LDS_AS char*)(const LDS_AS void*)sK(buf);
@@ -380,8 +378,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     using PF2 = std::integral_constant<int, 2>;
     using NOMASK = std::integral_constant<bool, false>;
     using MASKED = std::integral_constant<bool, true>;
-    using BUF0 = std::integral_constant<int, 0>;
-    using BUF1 = std::integral_constant<int, 1>;
 
     // Key tiles [lo, hi) of the current query tile, continuing the running state.
     auto run = [&](int lo, int hi) {
@@ -395,28 +391,13 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         int it = lo;
-        const int end_full = lo + n_full;
-        // Tiles that prefetch a full next tile (it + 1 < end_full), in pairs whose buffers are
-        // compile-time constants (0 then 1): the buffer choice then costs no address arithmetic.
-        // (Whole tiles only: in the split kernels the larger loop made the compiler keep arrays
-        // in scratch memory.)
-        if constexpr (!SPLIT) {
-            if ((it & 1) != 0 && it + 1 < end_full) {
-                step(PF1{}, NOMASK{}, it, BUF1{});
-                ++it;
-            }
-            for (; it + 2 < end_full; it += 2) {
-                step(PF1{}, NOMASK{}, it, BUF0{});
-                step(PF1{}, NOMASK{}, it + 1, BUF1{});
-            }
-        }
-        for (; it + 1 < end_full; ++it) step(PF1{}, NOMASK{}, it, it & 1);
+        for (; it + 1 < lo + n_full; ++it) step(PF1{}, NOMASK{}, it);
         if (n_full > 0) {
-            if (has_tail) step(PF2{}, NOMASK{}, it, it & 1);
-            else step(PF0{}, NOMASK{}, it, it & 1);
+            if (has_tail) step(PF2{}, NOMASK{}, it);
+            else step(PF0{}, NOMASK{}, it);
             ++it;
         }
-        if (has_tail) step(PF0{}, MASKED{}, it, it & 1);
+        if (has_tail) step(PF0{}, MASKED{}, it);
     };
 
     // Sets the coordinates of query tile `tile`, loads its Q^T fragments (held for the
