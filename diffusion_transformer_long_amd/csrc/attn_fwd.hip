@@ -338,10 +338,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // key ranges, 4% at 512 keys)
         if constexpr (PF == 1) load_tile(FULL{}, kv0 + kBlockN, buf ^ 1);
         if constexpr (PF == 2) load_tile(PARTIAL{}, kv0 + kBlockN, buf ^ 1);
-        // The two softmax blocks run at raised wave priority: when both waves of a SIMD can
-        // issue, the one with VALU work goes first and the other's MFMAs fill the matrix
-        // pipe behind it (measured 1-2% faster than equal priorities).
-        __builtin_amdgcn_s_setprio(1);
+        // All blocks run at equal wave priority.  (Raising it for the two softmax blocks was
+        // 1-2% faster while they formed a row max every half; with the lighter lane-sum
+        // softmax it is 1.6-2.2% slower at long key ranges.)
         s_half(s1, sk, 1);
         if constexpr (MASK) {  // keys past the end get weight 0
 #pragma unroll
@@ -365,7 +364,6 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const bool r1 = softmax_half(s1, p1, ls1, a1);
         asm volatile("" : "+v"(p1[0]), "+v"(p1[1]), "+v"(ls1));
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
         l_run += ls0 * a1 + ls1;
         if (r1) rescale_acc(a1);
         pv_half(p1, sv, 1);
