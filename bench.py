@@ -23,7 +23,9 @@ Legs timed in the same run and reported under "legs":
 Inputs are seeded synthetic tensors (no dataset, no weights) already resident in
 HBM when a timed region starts.  Times come from HIP events recorded on the stream
 the kernels are launched on.  "roofline" describes the headline kernel;
-"cpu_baseline" times the fp64 CPU oracle on a bounded sample of the headline workload.
+"cpu_baseline" times the fp64 CPU oracle over the whole headline workload on the host's
+cores, with each workload's oracle wall time beside it (c4 and c5 extrapolated from one
+head, or a block of its rows).
 """
 from __future__ import annotations
 
@@ -72,8 +74,8 @@ def parse():
     ap.add_argument("--no-headline", action="store_true",
                     help="skip the headline workload (for profiling one leg at a time); the JSON "
                          "line then carries the legs only, with value null")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-c5-rows", type=int, default=4096,
+                    help="rows of one Wan2.1-14B share head the oracle times (extrapolated)")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the attention kernel source hash and exit")
     return ap.parse_args()
@@ -126,27 +128,56 @@ def prewarm(torch, dev, seconds=1.0):
     del a
 
 
-def cpu_baseline(w, target_s):
+def _oracle_timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, c5_rows):
+    """The fp64 CPU oracle as it stands, timed on this host's cores: the whole headline
+    workload (every query row against every key), and beside it each workload's oracle
+    wall time (whole where it takes seconds; from one whole head, or a block of rows of
+    one head, extrapolated by flops where the whole would take minutes)."""
     import numpy as np
     import oracle
     import synthetic
     q, k, v = synthetic.workload_qkv(w)
-    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
-    per_row = 4.0 * w.Nkv * w.D
-    n = 256
-    t0 = time.perf_counter()
-    oracle.attn_rows(qd, kd, vd, synthetic.sample_rows(11, w.B, w.H, w.Nq, n))
-    dt = time.perf_counter() - t0
-    n2 = int(min(w.B * w.H * w.Nq, max(n, n * target_s / max(dt, 1e-3))))
-    rows = synthetic.sample_rows(12, w.B, w.H, w.Nq, n2)
-    t0 = time.perf_counter()
-    oracle.attn_rows(qd, kd, vd, rows)
-    dt = time.perf_counter() - t0
-    return {"value": per_row * len(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+    dt = _oracle_timed(lambda: oracle.attn(q, k, v))
+    per_config = {}
+    per_config[w.name] = {"oracle_s": round(dt, 3), "rows": "all %d" % (w.B * w.H * w.Nq),
+                          "tflops": round(w.flops / dt / 1e12, 5), "extrapolated": False}
+    err("[bench] oracle %s: %.2f s (whole)" % (w.name, dt))
+    tr = synthetic.TINY_RING
+    tq, tk, tv = synthetic.workload_qkv(tr)
+    t1 = _oracle_timed(lambda: oracle.attn(tq, tk, tv))
+    per_config[tr.name] = {"oracle_s": round(t1, 4), "rows": "all %d" % (tr.B * tr.H * tr.Nq),
+                           "tflops": round(tr.flops / t1 / 1e12, 5), "extrapolated": False}
+    r4 = synthetic.FLUX_RING4
+    q4 = q[:, r4.q_row0:r4.q_row0 + r4.Nq].contiguous()
+    t3 = _oracle_timed(lambda: oracle.attn(q4, k, v))
+    per_config[r4.name] = {"oracle_s": round(t3, 3), "rows": "all %d (rank 0's Q block)" % (r4.B * r4.H * r4.Nq),
+                           "tflops": round(r4.flops / t3 / 1e12, 5), "extrapolated": False}
+    del q, k, v, q4
+    for wl, nrows in ((synthetic.WAN5B, None), (synthetic.WAN14B_U8, c5_rows)):
+        a, b, c = synthetic.workload_qkv(wl)
+        a, b, c = (t.double().numpy() for t in (a, b, c))
+        n = wl.Nq if nrows is None else min(nrows, wl.Nq)
+        rows = np.stack([np.zeros(n, np.int64), np.zeros(n, np.int64), np.arange(n, dtype=np.int64)], axis=1)
+        t = _oracle_timed(lambda: oracle.attn_rows(a, b, c, rows))
+        scale = (wl.B * wl.H * wl.Nq) / n
+        per_config[wl.name] = {
+            "oracle_s": round(t * scale, 1), "extrapolated": True,
+            "measured": "%s of head 0 (each against all %d keys) in %.2f s, x%.1f by flops"
+                        % ("all %d rows" % n if n == wl.Nq else "rows 0..%d" % (n - 1), wl.Nkv, t, scale),
+            "tflops": round(wl.flops / scale / t / 1e12, 5)}
+        err("[bench] oracle %s: %s" % (wl.name, per_config[wl.name]))
+        del a, b, c
+    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": "%d query rows (seeded, of %d) of the %s workload, each against all %d keys, "
-                      "fp64; %.1f s" % (len(rows), w.B * w.H * w.Nq, w.name, w.Nkv, dt),
-            "cpu_model": _cpu_model()}
+            "sample": "the whole %s workload: all %d query rows against all %d keys, fp64, %.2f s"
+                      % (w.name, w.B * w.H * w.Nq, w.Nkv, dt),
+            "cpu_model": _cpu_model(), "per_config": per_config}
 
 
 def _cpu_model():
@@ -405,7 +436,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.no_headline:
         err("[bench] cpu baseline (oracle on host cores)")
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_c5_rows)
         err("[bench] cpu baseline: %s" % cpu)
 
     line = {

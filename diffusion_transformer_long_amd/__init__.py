@@ -16,9 +16,10 @@ Entry points (same names as the C ABI):
   qkv_norm_rope_permute(x, gamma_q, gamma_k, cos, sin, p, ...) -> out
   attn_fwd_lse_kv_chunks(q, k, v, chunks) -> (o_parts, lse_parts)  all KV chunks, one launch
 and a driver that only sequences those calls:
-  ring_attention(q, k, v, chunks)          -> (o, lse)              per-round partials (or
-                                                                    one launch), then the
-                                                                    merge; or rounds accumulated
+  ring_attention(q, k, v, chunks)          -> (o, lse)              the rounds' partials (one
+                                                                    launch or one per round),
+                                                                    then the merge; or rounds
+                                                                    accumulated
 """
 from __future__ import annotations
 
@@ -330,20 +331,30 @@ def attn_fwd_lse_kv_chunks(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ch
     return o_parts, lse_parts
 
 
+def _round_fills_gpu(q: torch.Tensor) -> bool:
+    """Whether one round's launch (the 128-row query tiles of q, two per compute unit)
+    occupies every workgroup slot of the GPU."""
+    B, Nq, H, _ = q.shape
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return B * H * ((Nq + 127) // 128) >= 2 * cus
+
+
 def ring_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: int,
                    out_dtype: torch.dtype = torch.bfloat16, softmax_scale: Optional[float] = None,
                    o_parts: Optional[torch.Tensor] = None, lse_parts: Optional[torch.Tensor] = None,
                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    accumulate: bool = False, o_acc: Optional[torch.Tensor] = None,
-                   one_launch: bool = False,
+                   one_launch: Optional[bool] = None,
                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention over all keys computed as Ring attention's rounds on one GPU, over
     contiguous KV chunks [t*C, (t+1)*C) (B must be 1 for the per-round forms, whose
     chunks are views of k and v).
 
-    accumulate=False: one attn_fwd_lse call per round into f32 partials (o_parts,
-    lse_parts), then the LSE merge; with one_launch=True the partials of all rounds come
-    from one attn_fwd_lse_kv_chunks call (any B).
+    accumulate=False: f32 partials of every round (o_parts, lse_parts), then the LSE
+    merge.  The partials come from one attn_fwd_lse call per round (one_launch=False),
+    or from one attn_fwd_lse_kv_chunks call for all rounds (one_launch=True, any B);
+    by default the one launch is taken when a single round's tiles would leave workgroup
+    slots idle (short Q blocks such as the FLUX Ring-4 share), one call per round otherwise.
     accumulate=True: the first round writes an f32 running result (o_acc, and lse), each
     later round folds its chunk into it with attn_fwd_lse_accumulate, and the last round
     writes the final o in out_dtype; no partials are stored."""
@@ -351,6 +362,8 @@ def ring_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunks: in
     Nkv = k.shape[1]
     if chunks <= 0 or Nkv % chunks != 0:
         raise ValueError("chunks must be positive and divide Nkv")
+    if one_launch is None:
+        one_launch = chunks > 1 and not _round_fills_gpu(q)
     if not accumulate and one_launch:
         o_parts, lse_parts = attn_fwd_lse_kv_chunks(q, k, v, chunks, o_parts, lse_parts,
                                                     softmax_scale, stream=stream)

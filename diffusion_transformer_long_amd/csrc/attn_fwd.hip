@@ -89,7 +89,8 @@ constexpr float kMaxLaneSum = pow2_int((int)kRescaleThreshold);
 // reference moves again (peaked FLUX-like rows: 6% faster on 1152-key Ring chunks).
 constexpr float kHeadroom = 4.0f;
 // A tile's finaliser polls its helpers' flags at most this often (s_sleep 8 between
-// polls, ~0.2 us; the bound is ~4 ms), then computes the missing keys itself.
+// polls, ~0.2 us; the bound is ~4 ms), then computes the missing keys itself.  The host
+// may lower the bound (DTL_ATTN_MAX_POLLS), which changes only who computes those keys.
 constexpr int kMaxPolls = 20000;
 
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -587,7 +588,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     // the helpers run concurrently and finish their pieces about now: poll,
                     // but only for a bounded time
                     int ok = 0;
-                    for (int poll = 0; poll < kMaxPolls && !ok; ++poll) {
+                    for (int poll = 0; poll < work.max_polls && !ok; ++poll) {
                         ok = 1;
                         for (int gg = g_first; gg <= g_last; ++gg)
                             ok &= __hip_atomic_load(work.flag + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == work.epoch;
@@ -761,6 +762,14 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // keys) those costs exceed the idle tail.
     StreamK work = plan_stream_k(tiles, n_kv, slots);
     work.slots = (int)slots;
+    // DTL_ATTN_MAX_POLLS (tests) lowers the finalisers' wait for their helpers; at 0 each
+    // finaliser computes the rest of its tile itself.  Like the two variables above it
+    // changes who computes which keys, never the result.
+    work.max_polls = kMaxPolls;
+    if (const char* env = getenv("DTL_ATTN_MAX_POLLS")) {
+        const long want = strtol(env, nullptr, 10);
+        if (want >= 0 && want < kMaxPolls) work.max_polls = (int)want;
+    }
     // a workspace is needed only when some split range starts inside a tile
     bool split = false;
     for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;

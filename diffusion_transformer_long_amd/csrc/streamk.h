@@ -20,10 +20,13 @@
 //     inside it (a range's last)       (bounded) for the flags of the workgroups that own
 //                                      the rest of the tile, folds in their states and
 //                                      writes O and LSE.
-// A finaliser only waits for split workgroups with higher ids, which are dispatched
-// after it and need nothing from anyone before publishing.  If a flag does not carry the
-// epoch within the bound, the finaliser computes the rest of the tile itself: the result
-// never depends on timing and every wave terminates.
+// A finaliser only waits for workgroups that need nothing from anyone before publishing,
+// but nothing guarantees that they are resident at the same time: the workgroup ids are
+// remapped to XCD-contiguous ranges, so a helper can be dispatched after its finaliser,
+// and another stream or process can hold the compute units it would need.  The wait is
+// therefore bounded (max_polls polls of the flags): if a flag does not carry the epoch
+// in time, the finaliser computes the rest of the tile itself.  The result never depends
+// on timing and every wave terminates.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,6 +44,7 @@ struct StreamK {
     unsigned long long* flag;   // [G_sk]
     unsigned long long epoch;   // this launch's flag value
     int slots;                  // resident workgroups the schedule assumes (whole-tile grid bound)
+    int max_polls;              // a finaliser's bound on polls of its helpers' flags (0: none)
 };
 
 // First unit of split-part workgroup g (g = G_sk gives W).

@@ -1,7 +1,8 @@
 """GPU parity of attn_merge_lse and the three Ulysses permutes.
 
-Merge: Ring equivalence on GPU partials; the merge alone fed oracle partials (rounded
-to f32) against the oracle's merge of the same values; P = 1 identity; an empty
+Merge: Ring equivalence on GPU partials; the merge alone fed f32 partials against the
+oracle's merge of the same values (f32 output within the f32 error; bf16 output within
+half a bf16 ulp plus that error and >= 99% correctly rounded); P = 1 identity; an empty
 (-inf) part; all parts empty; order of parts; bf16 partials.
 Permutes (seq->head, head->seq, fused QKV seq->head): bit-exact against the oracle's
 index maps for bf16/f32/1-byte/8-byte elements, 16-byte and narrower copy units, p = 1,
@@ -16,7 +17,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_helpers import assert_close, log, to_np
+from gpu_helpers import assert_bf16_rounding_of, assert_close, log, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +42,15 @@ def test_merge_alone_matches_oracle(P, B, N, H, D, out_dtype):
                                 out_dtype=out_dtype)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.merge(o_p, l_p)
-    tol = 1e-5 if out_dtype == torch.float32 else 1e-2
-    assert_close("merged O", to_np(o), o_ref, max_abs=tol * 4, mean_abs=tol)
+    # The kernel works in f32: weights exp(lse_t - L) with a few ulps of relative error
+    # (arguments up to ~30 in magnitude), then a sum of P weighted parts.  Its absolute
+    # error is below 2^-17 times the largest |o_t| of the element (about 8 ulps of f32
+    # relative error at P = 8, with margin).
+    f32_err = 2.0 ** -17 * np.abs(o_p).max(axis=0).astype(np.float64)
+    if out_dtype == torch.float32:
+        assert_close("merged O", to_np(o), o_ref, max_abs=float(f32_err.max()), mean_abs=1e-6)
+    else:
+        assert_bf16_rounding_of("merged O (bf16)", to_np(o), o_ref, f32_err)
     assert_close("merged LSE", to_np(lse), l_ref, max_abs=1e-5, mean_abs=1e-6)
 
 

@@ -4,7 +4,10 @@ On the real GPU only large workloads reach it (more tiles than workgroup slots, 
 remainder, at least 64 key blocks per tile: Wan2.2-5B).  DTL_ATTN_SLOTS schedules as if the
 GPU held fewer workgroups, which makes small shapes take the same path: whole tiles for
 the first rounds, the remainder's 64-key blocks spread over the slots, pieces published
-to the workspace and folded in by each tile's finaliser.  The cases cover a tile split
+to the workspace and folded in by each tile's finaliser.  With DTL_ATTN_MAX_POLLS=0 every
+finaliser gives up on its helpers at once and computes the rest of its tile itself (the
+path taken when helpers are not resident in time); those runs must give the same result.
+The cases cover a tile split
 over 8 workgroups, ranges crossing tile boundaries, the ragged last key block inside a
 split tile, B = 2, D = 64 and 128, 4- and 8-wave workgroups (DTL_ATTN_WAVES), bf16 and
 f32 outputs, and the accumulate entry point with rows that hold no keys yet.  Every result
@@ -36,6 +39,21 @@ def slots():
         os.environ.pop("DTL_ATTN_SLOTS", None)
     else:
         os.environ["DTL_ATTN_SLOTS"] = old
+
+
+@pytest.fixture
+def polls():
+    """DTL_ATTN_MAX_POLLS: how often a tile's finaliser polls its helpers' flags before it
+    computes the rest of the tile itself (0: at once)."""
+    old = os.environ.get("DTL_ATTN_MAX_POLLS")
+
+    def set_polls(n):
+        os.environ["DTL_ATTN_MAX_POLLS"] = str(n)
+    yield set_polls
+    if old is None:
+        os.environ.pop("DTL_ATTN_MAX_POLLS", None)
+    else:
+        os.environ["DTL_ATTN_MAX_POLLS"] = old
 
 
 @pytest.fixture
@@ -166,3 +184,88 @@ def test_split_schedule_repeated_calls_agree(slots):
     for o, lse in outs:
         assert_close("O", to_np(o), o_ref)
         assert_close("LSE", to_np(lse), l_ref)
+
+
+# (waves, slots, B, Nq, Nkv, H, D, k_scale): the split cases of both workgroup sizes
+FALLBACK_CASES = [(4,) + c for c in CASES[:4]] + [(8,) + c for c in CASES8[:3]]
+
+
+@pytest.mark.parametrize("case", FALLBACK_CASES, ids=lambda c: "w%d_slots%d_B%d_Nq%d_Nkv%d_H%d_D%d" % c[:7])
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_split_finaliser_fallback_matches_oracle(slots, waves, polls, case, o_dtype):
+    """Every finaliser computes the keys its helpers own itself (no wait): same result."""
+    import diffusion_transformer_long_amd as dtl
+    nw, n, B, Nq, Nkv, H, D, ks = case
+    log("split finaliser fallback, %d waves, slots=%d %s o=%s" % (nw, n, case[2:], o_dtype))
+    q, k, v = _inputs(7000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
+    slots(n)
+    if D == 128:
+        waves(nw)
+    polls(0)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attn(q, k, v)
+    assert_close("O", to_np(o), o_ref)
+    assert_close("LSE", to_np(lse), l_ref)
+    # the fallback runs the same arithmetic on the finaliser's own keys in the same order
+    # as the helpers would, but folds no published state: compare with the waiting path
+    os.environ.pop("DTL_ATTN_MAX_POLLS")
+    o2, lse2 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    assert_close("O vs waiting path", to_np(o), to_np(o2))
+
+
+@pytest.mark.parametrize("nw", [4, 8])
+def test_split_finaliser_fallback_accumulate(slots, waves, polls, nw):
+    """attn_fwd_lse_accumulate through the split schedule with every finaliser computing
+    its whole tile, rows without previous keys included."""
+    import diffusion_transformer_long_amd as dtl
+    B, Nq, Np, Nkv, H, D = 1, 1152, 300, 4100, 1, 128
+    g = np.random.Generator(np.random.PCG64(78))
+    q = synthetic.to_bf16(g.standard_normal((B, Nq, H, D), dtype=np.float32))
+    kp = synthetic.to_bf16(g.standard_normal((B, Np, H, D), dtype=np.float32))
+    vp = synthetic.to_bf16(g.standard_normal((B, Np, H, D), dtype=np.float32))
+    k = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32) * np.float32(2.0))
+    v = synthetic.to_bf16(g.standard_normal((B, Nkv, H, D), dtype=np.float32))
+    o_p, l_p = oracle.attn(q, kp, vp)
+    o_p32, l_p32 = o_p.astype(np.float32), l_p.astype(np.float32)
+    empty = np.arange(Nq) % 7 == 3
+    l_p32[:, :, empty] = -np.inf
+    o_p32[:, empty] = np.nan
+    o_c, l_c = oracle.attn(q, k, v)
+    o_ref, l_ref = oracle.merge(np.stack([np.nan_to_num(o_p32.astype(np.float64)), o_c]),
+                                np.stack([l_p32.astype(np.float64), l_c]))
+    slots(8 if nw == 4 else 4)
+    waves(nw)
+    polls(0)
+    for o_dtype in (torch.float32, torch.bfloat16):
+        o, lse = dtl.attn_fwd_lse_accumulate(q.to(DEV), k.to(DEV), v.to(DEV),
+                                             torch.from_numpy(o_p32).to(DEV), torch.from_numpy(l_p32).to(DEV),
+                                             o_dtype=o_dtype)
+        torch.cuda.synchronize()
+        assert_close("O %s" % o_dtype, to_np(o), o_ref)
+        assert_close("LSE", to_np(lse), l_ref)
+
+
+def test_split_calls_on_two_streams_at_once(slots):
+    """Split-schedule calls on two streams of equal (default) priority, enqueued
+    alternately so that they overlap: each takes its own workspace from the pool and
+    carries its own launch counter value, so both match the oracle."""
+    import diffusion_transformer_long_amd as dtl
+    slots(8)
+    ins = [_inputs(95 + i, 1, 1152, 4100, 1, 128, 2.0 + i) for i in range(2)]
+    dev_ins = [tuple(t.to(DEV) for t in x) for x in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    outs = [[], []]
+    for rep in range(4):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                outs[i].append(dtl.attn_fwd_lse(*dev_ins[i], o_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for i in range(2):
+        o_ref, l_ref = oracle.attn(*ins[i])
+        for o, lse in outs[i]:
+            assert_close("stream %d O" % i, to_np(o), o_ref)
+            assert_close("stream %d LSE" % i, to_np(lse), l_ref)

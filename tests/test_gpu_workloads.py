@@ -1,16 +1,23 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the bench times.
 
-* tiny ring (N=256, 4 heads of 64, KV 4 x 64): full oracle; one full-sequence call and
+Where the oracle finishes in seconds it is run over the whole workload and every output
+element is compared; the two long sequences, whose full oracle would take minutes, are
+compared on whole query tiles plus a seeded row sample.
+
+* tiny ring (N=256, 4 heads of 64, KV 4 x 64): whole oracle; one full-sequence call and
   the ring emulation (4 chunk calls + merge).
-* FLUX (N=4608, 24 x 128, K x 3): full-sequence call; a seeded sample of query rows
-  (first and last row of every head included) against the oracle row by row.
-* FLUX Ring-4 share: each of the 4 ranks' 1152-row Q blocks against the full K/V as
-  4 chunks of 1152 + merge, sampled rows; the Ulysses-4 permute of the four Q shards
-  [4,1,1152,24,128] -> [4,1,4608,6,128], bit-exact over the whole tensor.
-* Wan2.2-5B (N=27280, 24 x 128): full-sequence call, sampled rows.
-* Wan2.1-14B Ulysses-8 share (N=75600, 5 x 128, KV 8 x 9450): chunks + merge, sampled rows.
-* Wan2.2 cross-attention (27280 video queries x 512 text keys, 24 x 128): full call, sampled
-  rows, bf16 and f32 outputs.
+* FLUX (N=4608, 24 x 128, K x 3): whole oracle, all 110592 rows, bf16 and f32 outputs.
+* FLUX Ring-4 share: all four ranks' 1152-row Q blocks against the full K/V as 4 chunks of
+  1152, every row, in the three forms (one attn_fwd_lse call per round + merge; all rounds'
+  partials from one attn_fwd_lse_kv_chunks launch + merge; rounds accumulated in place);
+  the one-launch partials themselves against the oracle over each chunk; the Ulysses-4
+  permute of the four Q shards [4,1,1152,24,128] -> [4,1,4608,6,128], bit-exact.
+* Wan2.2-5B (N=27280, 24 x 128): whole first and ragged last query tiles of every head,
+  every query tile of the split (stream-K) part of the schedule, and a seeded row sample.
+* Wan2.1-14B Ulysses-8 share (N=75600, 5 x 128, KV 8 x 9450): chunks + merge; whole first
+  and ragged last tiles of every head, and a seeded row sample.
+* Wan2.2 cross-attention (27280 video queries x 512 text keys, 24 x 128): whole oracle,
+  bf16 and f32 outputs.
 """
 import numpy as np
 import pytest
@@ -24,16 +31,66 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 SAMPLE_ROWS = 2048
+TILE = 256   # query rows of the 8-wave workgroups these long workloads run on
 
 
-def _check_rows(name, w, o, lse, q, k, v, n=SAMPLE_ROWS, seed=0):
-    rows = synthetic.sample_rows(seed or w.seed + 100, w.B, w.H, w.Nq, n)
+def _bnhd(idx):
+    b, i, h = idx[:3]
+    return "b=%d row=%d head=%d" % (b, i, h) + (" d=%d" % idx[3] if len(idx) > 3 else "")
+
+
+def _bhn(idx):
+    return "b=%d head=%d row=%d" % tuple(idx)
+
+
+def _check_full(name, o, lse, o_ref, l_ref, row0=0):
+    """Every element of o [B,N,H,D] and lse [B,H,N] against the oracle; row labels are
+    offset by row0 (a share's first row in the full sequence)."""
+    off = lambda f: (lambda idx: f((idx[0], idx[1] + row0) + tuple(idx[2:])))
+    offl = lambda f: (lambda idx: f((idx[0], idx[1], idx[2] + row0)))
+    assert_close(name + " O", to_np(o), o_ref, labels=off(_bnhd))
+    assert_close(name + " LSE", to_np(lse), l_ref, labels=offl(_bhn))
+
+
+def _check_rows(name, o, lse, q, k, v, rows):
+    """Rows (b, h, i) of o and lse against the oracle computed for those rows alone."""
+    rows = np.asarray(rows, np.int64).reshape(-1, 3)
     o_ref, l_ref = oracle.attn_rows(q, k, v, rows)
     b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
     o_np = o.float().cpu().numpy()
     l_np = lse.cpu().numpy()
-    assert_close(name + " O (%d rows)" % len(rows), o_np[b, i, h].astype(np.float64), o_ref)
-    assert_close(name + " LSE (%d rows)" % len(rows), l_np[b, h, i].astype(np.float64), l_ref)
+    lab_o = lambda idx: "b=%d row=%d head=%d d=%d" % (b[idx[0]], i[idx[0]], h[idx[0]], idx[1])
+    lab_l = lambda idx: "b=%d row=%d head=%d" % (b[idx[0]], i[idx[0]], h[idx[0]])
+    assert_close(name + " O (%d rows)" % len(rows), o_np[b, i, h].astype(np.float64), o_ref, labels=lab_o)
+    assert_close(name + " LSE (%d rows)" % len(rows), l_np[b, h, i].astype(np.float64), l_ref, labels=lab_l)
+
+
+def _tile_rows(B, H, Nq, tiles):
+    """(b, h, i) of every row of the given (b, h, first row) query tiles, sorted."""
+    out = set()
+    for b, h, r0 in tiles:
+        for i in range(r0, min(r0 + TILE, Nq)):
+            out.add((b, h, i))
+    return np.asarray(sorted(out), np.int64).reshape(-1, 3)
+
+
+def _split_tiles(B, Nq, Nkv, H):
+    """The query tiles (b, h, first row) of the attention schedule's split (stream-K)
+    part for a long-key workload on this GPU: with one 256-row workgroup per compute unit,
+    the tiles past the last complete round when that remainder is at most a quarter of
+    the slots and the tiles have at least 64 key blocks (the library's rule)."""
+    slots = torch.cuda.get_device_properties(DEV).multi_processor_count
+    n_qt = (Nq + TILE - 1) // TILE
+    tiles = n_qt * H * B
+    n_kv = (Nkv + 63) // 64
+    rem = tiles % slots
+    if not (tiles >= slots and 0 < rem and rem * 4 <= slots and n_kv >= 64):
+        return []
+    out = []
+    for t in range(tiles - rem, tiles):
+        bh, qt = divmod(t, n_qt)
+        out.append((bh // H, bh % H, qt * TILE))
+    return out
 
 
 def test_tiny_ring_full_oracle():
@@ -44,41 +101,68 @@ def test_tiny_ring_full_oracle():
     o_ref, l_ref = oracle.attn(q, k, v)
     o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
-    assert_close("full call O", to_np(o), o_ref)
-    assert_close("full call LSE", to_np(lse), l_ref)
+    _check_full("full call", o, lse, o_ref, l_ref)
     o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
     torch.cuda.synchronize()
-    assert_close("ring 4x64 O", to_np(o), o_ref)
-    assert_close("ring 4x64 LSE", to_np(lse), l_ref)
+    _check_full("ring 4x64", o, lse, o_ref, l_ref)
 
 
-def test_flux_full_sequence():
+@pytest.fixture(scope="module")
+def flux():
+    """FLUX's tensors and the oracle over the whole sequence (every row, every head)."""
+    q, k, v = synthetic.workload_qkv(synthetic.FLUX)
+    log("oracle: FLUX, all %d rows" % (q.shape[1] * q.shape[2]))
+    o_ref, l_ref = oracle.attn(q, k, v)
+    return q, k, v, o_ref, l_ref
+
+
+def test_flux_full_sequence_every_row(flux):
     import diffusion_transformer_long_amd as dtl
     w = synthetic.FLUX
     log("workload %s" % w.name)
-    q, k, v = synthetic.workload_qkv(w)
+    q, k, v, o_ref, l_ref = flux
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o, lse = dtl.attn_fwd_lse(qd, kd, vd)
     torch.cuda.synchronize()
-    _check_rows("flux", w, o, lse, q, k, v, n=8192)
+    _check_full("flux bf16-out", o, lse, o_ref, l_ref)
     # max|O| reaches 4 here, where one bf16 rounding alone can cost 0.0156: judge the
     # kernel's arithmetic with an f32 output as well
     o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    _check_rows("flux f32-out", w, o32, lse32, q, k, v, n=8192)
+    _check_full("flux f32-out", o32, lse32, o_ref, l_ref)
 
 
-def test_flux_ring4_share_and_ulysses4_permute():
+def test_flux_ring4_share_every_rank_every_form(flux):
     import diffusion_transformer_long_amd as dtl
     w = synthetic.FLUX_RING4
     log("workload %s" % w.name)
-    qf, k, v = synthetic.workload_qkv(synthetic.FLUX)   # the share reuses FLUX's tensors
+    qf, k, v, o_ref, l_ref = flux        # the share reuses FLUX's tensors
     kd, vd = k.to(DEV), v.to(DEV)
+    C = w.chunk_len
+    # the oracle over each key chunk, for the one-launch partials (every rank's rows)
+    part_ref = [oracle.attn(qf, k[:, t * C:(t + 1) * C], v[:, t * C:(t + 1) * C]) for t in range(w.chunks)]
     for rank in range(4):
-        q = qf[:, rank * w.Nq:(rank + 1) * w.Nq].contiguous()
-        o, lse = dtl.ring_attention(q.to(DEV), kd, vd, w.chunks)
+        r0 = rank * w.Nq
+        q = qf[:, r0:r0 + w.Nq].contiguous()
+        qd = q.to(DEV)
+        ref_o, ref_l = o_ref[:, r0:r0 + w.Nq], l_ref[:, :, r0:r0 + w.Nq]
+        log("rank %d (rows %d..%d)" % (rank, r0, r0 + w.Nq - 1))
+        o, lse = dtl.ring_attention(qd, kd, vd, w.chunks)
         torch.cuda.synchronize()
-        _check_rows("ring4 rank%d" % rank, w, o, lse, q, k, v, n=1024, seed=300 + rank)
+        _check_full("rank%d default" % rank, o, lse, ref_o, ref_l, row0=r0)
+        o, lse = dtl.ring_attention(qd, kd, vd, w.chunks, one_launch=False)
+        torch.cuda.synchronize()
+        _check_full("rank%d per-round calls" % rank, o, lse, ref_o, ref_l, row0=r0)
+        o_p, l_p = dtl.attn_fwd_lse_kv_chunks(qd, kd, vd, w.chunks)
+        o, lse = dtl.attn_merge_lse(o_p, l_p)
+        torch.cuda.synchronize()
+        _check_full("rank%d one launch + merge" % rank, o, lse, ref_o, ref_l, row0=r0)
+        for t in range(w.chunks):
+            _check_full("rank%d part %d" % (rank, t), o_p[t], l_p[t], part_ref[t][0][:, r0:r0 + w.Nq],
+                        part_ref[t][1][:, :, r0:r0 + w.Nq], row0=r0)
+        o, lse = dtl.ring_attention(qd, kd, vd, w.chunks, accumulate=True)
+        torch.cuda.synchronize()
+        _check_full("rank%d accumulated" % rank, o, lse, ref_o, ref_l, row0=r0)
     shards = qf.reshape(1, 4, w.Nq, w.H, w.D).transpose(0, 1).contiguous()   # [4,1,1152,24,128]
     out = dtl.seq_to_head_permute(shards.to(DEV), 4)
     torch.cuda.synchronize()
@@ -88,14 +172,21 @@ def test_flux_ring4_share_and_ulysses4_permute():
     log("  permute [4,1,1152,24,128] -> [4,1,4608,6,128] bit-exact")
 
 
-def test_wan22_5b_full_sequence():
+def test_wan22_5b_whole_tiles():
     import diffusion_transformer_long_amd as dtl
     w = synthetic.WAN5B
     log("workload %s" % w.name)
     q, k, v = synthetic.workload_qkv(w)
     o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV))
     torch.cuda.synchronize()
-    _check_rows("wan5b", w, o, lse, q, k, v)
+    last = (w.Nq - 1) // TILE * TILE
+    split = _split_tiles(w.B, w.Nq, w.Nkv, w.H)
+    log("  split-part tiles on this GPU: %s" % [(h, r0) for _, h, r0 in split])
+    assert split, "Wan2.2-5B no longer reaches the split schedule: choose other tiles"
+    first_last = [(0, h, 0) for h in range(w.H)] + [(0, h, last) for h in range(w.H)]
+    _check_rows("wan5b first+last tiles", o, lse, q, k, v, _tile_rows(w.B, w.H, w.Nq, first_last))
+    _check_rows("wan5b split tiles", o, lse, q, k, v, _tile_rows(w.B, w.H, w.Nq, split))
+    _check_rows("wan5b sample", o, lse, q, k, v, synthetic.sample_rows(w.seed + 100, w.B, w.H, w.Nq, SAMPLE_ROWS))
 
 
 def test_wan21_14b_ulysses8_share_kv8_merge():
@@ -105,7 +196,10 @@ def test_wan21_14b_ulysses8_share_kv8_merge():
     q, k, v = synthetic.workload_qkv(w)
     o, lse = dtl.ring_attention(q.to(DEV), k.to(DEV), v.to(DEV), w.chunks)
     torch.cuda.synchronize()
-    _check_rows("wan14b u8", w, o, lse, q, k, v, n=1024)
+    last = (w.Nq - 1) // TILE * TILE
+    tiles = [(0, h, 0) for h in range(w.H)] + [(0, h, last) for h in range(w.H)]
+    _check_rows("wan14b u8 first+last tiles", o, lse, q, k, v, _tile_rows(w.B, w.H, w.Nq, tiles))
+    _check_rows("wan14b u8 sample", o, lse, q, k, v, synthetic.sample_rows(w.seed + 100, w.B, w.H, w.Nq, 1024))
 
 
 def test_wan22_cross_attention_512_text_keys():
@@ -117,5 +211,6 @@ def test_wan22_cross_attention_512_text_keys():
     o, lse = dtl.attn_fwd_lse(qd, kd, vd)
     o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    _check_rows("cross", w, o, lse, q, k, v)
-    _check_rows("cross f32-out", w, o32, lse32, q, k, v)
+    o_ref, l_ref = oracle.attn(q, k, v)
+    _check_full("cross bf16-out", o, lse, o_ref, l_ref)
+    _check_full("cross f32-out", o32, lse32, o_ref, l_ref)
