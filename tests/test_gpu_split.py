@@ -208,12 +208,14 @@ def test_split_finaliser_fallback_matches_oracle(slots, waves, polls, case, o_dt
     o_ref, l_ref = oracle.attn(q, k, v)
     assert_close("O", to_np(o), o_ref)
     assert_close("LSE", to_np(lse), l_ref)
-    # the fallback runs the same arithmetic on the finaliser's own keys in the same order
-    # as the helpers would, but folds no published state: compare with the waiting path
+    # the waiting path (helper states folded in) on the same inputs, also against the
+    # oracle: the two round their bf16 weights against different running maxima, so they
+    # agree with each other only to the parity bar, not bitwise
     os.environ.pop("DTL_ATTN_MAX_POLLS")
     o2, lse2 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=o_dtype)
     torch.cuda.synchronize()
-    assert_close("O vs waiting path", to_np(o), to_np(o2))
+    assert_close("O, waiting path", to_np(o2), o_ref)
+    assert_close("LSE, waiting path", to_np(lse2), l_ref)
 
 
 @pytest.mark.parametrize("nw", [4, 8])
