@@ -8,6 +8,7 @@ library has not been built; there is no fallback.
 
 Entry points (same names as the C ABI):
   attn_fwd_lse(q, k, v, ...)            -> (o, lse)
+  attn_fwd_lse_noalloc(q, k, v, o, lse)  -> (o, lse)  nothing allocated, outputs given
   attn_fwd_lse_accumulate(q, k, v, o_prev, lse_prev, ...) -> (o, lse)
   attn_merge_lse(o_parts, lse_parts, ...) -> (o, lse)
   seq_to_head_permute(x, p, ...)        -> out
@@ -33,10 +34,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdtl.so")
 
-DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP = 0, 1, 2, 3
+DTL_OK, DTL_ERR_INVALID_ARG, DTL_ERR_UNSUPPORTED, DTL_ERR_HIP, DTL_ERR_WORKSPACE = 0, 1, 2, 3, 4
 DTL_BF16, DTL_F32 = 0, 1
 
-EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_accumulate", "attn_fwd_lse_kv_chunks", "attn_merge_lse",
+EXPORTS = ("attn_fwd_lse", "attn_fwd_lse_noalloc", "attn_fwd_lse_accumulate", "attn_fwd_lse_kv_chunks", "attn_merge_lse",
            "seq_to_head_permute", "head_to_seq_permute", "qkv_seq_to_head_permute",
            "qkv_norm_rope_permute", "dtl_status_string")
 
@@ -56,6 +57,8 @@ def _load_library():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_lse.restype = i
+    lib.attn_fwd_lse_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_lse_noalloc.restype = i
     lib.attn_fwd_lse_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_lse_accumulate.restype = i
     lib.attn_fwd_lse_kv_chunks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
@@ -132,6 +135,29 @@ def attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     _check(lib.attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Nq, Nkv, H, D, scale, _dtype_code(o.dtype), _stream(q, stream)))
+    return o, lse
+
+
+def attn_fwd_lse_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                         lse: torch.Tensor, softmax_scale: Optional[float] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_fwd_lse for callers that cannot allocate: the caller passes o (bf16 or f32)
+    and lse; the library's split workspace is a static device array shared by every call
+    on the device (calls that overlap in time on one device race)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.bfloat16, 4)
+    B, Nq, H, D = q.shape
+    Nkv = k.shape[1]
+    if tuple(k.shape) != (B, Nkv, H, D) or tuple(v.shape) != (B, Nkv, H, D):
+        raise ValueError("k and v must be [B, Nkv, H, D] matching q %s" % (tuple(q.shape),))
+    _dev(o, "o", None, 4)
+    _dev(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Nq, H, D) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must be [B,Nq,H,D] and lse [B,H,Nq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib.attn_fwd_lse_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, Nq, Nkv, H, D, scale, _dtype_code(o.dtype),
+                                    _stream(q, stream)))
     return o, lse
 
 

@@ -686,14 +686,29 @@ void launch_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, vo
         launch_d<D, NW, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
 }
 
-// Per-device launch facts: compute units and a memory pool for the stream-ordered
-// workspace.
+// Static workspace of attn_fwd_lse_noalloc: the states and flags of the split pieces, for
+// callers that may not allocate.  Sized for the largest split part on a 256-CU MI355X
+// (at most 512 workgroups of 256 threads or 256 of 512, 64 f32 accumulators and 4 f32 of
+// running max and sum per thread at head_dim 128, and one 8-byte flag per workgroup);
+// a schedule needing more is rejected before launch.  Each device holds its own copy
+// until the process ends.  In host code `scratch` only names the symbol: its device
+// address comes from hipGetSymbolAddress (DeviceInfo::scratch).
+constexpr size_t kScratchBytes = 36u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Per-device launch facts: compute units, the address of this device's copy of
+// `scratch`, and (created at the first call that needs it) a memory pool for the
+// stream-ordered workspace.
 struct DeviceInfo {
     int cus = 0;
+    char* scratch = nullptr;
+    hipError_t scratch_err = hipSuccess;
     hipMemPool_t pool = nullptr;
 };
 
-hipError_t device_info(DeviceInfo** out) {
+// Sets *out to the current device's facts, gathering them on its first call there (with
+// that device current).  With want_pool, also creates the device's pool if it has none.
+hipError_t device_info(DeviceInfo** out, bool want_pool) {
     static std::mutex mu;
     static DeviceInfo infos[64];
     int dev = 0;
@@ -706,16 +721,26 @@ hipError_t device_info(DeviceInfo** out) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        void* p = nullptr;
+        d.scratch_err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        d.scratch = d.scratch_err == hipSuccess ? static_cast<char*>(p) : nullptr;
+        d.cus = cus;
+    }
+    if (want_pool && d.pool == nullptr) {
         hipMemPoolProps props = {};
         props.allocType = hipMemAllocationTypePinned;
         props.location.type = hipMemLocationTypeDevice;
         props.location.id = dev;
-        e = hipMemPoolCreate(&d.pool, &props);
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
         if (e != hipSuccess) return e;
         uint64_t keep = UINT64_MAX;   // keep freed workspace in the pool for the next call
-        e = hipMemPoolSetAttribute(d.pool, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess) return e;
-        d.cus = cus;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            hipMemPoolDestroy(pool);
+            return e;
+        }
+        d.pool = pool;
     }
     *out = &d;
     return hipSuccess;
@@ -725,14 +750,16 @@ hipError_t device_info(DeviceInfo** out) {
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
-                           int H, int D, int P, float scale, bool out_f32, hipStream_t stream) {
+                           int H, int D, int P, float scale, bool out_f32, bool static_ws,
+                           bool* ws_too_small, hipStream_t stream) {
     // P > 1: P equal key chunks of Nkv / P keys each, one result per (chunk, batch), as
     // if the chunks were P * B batches sharing the batch's queries
     const int Bq = B;
     B *= P;
     Nkv /= P;
+    if (ws_too_small != nullptr) *ws_too_small = false;
     DeviceInfo* dev = nullptr;
-    hipError_t e = device_info(&dev);
+    hipError_t e = device_info(&dev, false);
     if (e != hipSuccess) return e;
     // DTL_ATTN_SLOTS (tests, tuning) schedules as if the GPU held that many workgroups; it
     // changes which tiles are split, never the result.  It may only lower the count.
@@ -773,17 +800,33 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // a workspace is needed only when some split range starts inside a tile
     bool split = false;
     for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;
-    void* ws = nullptr;
+    void* ws = nullptr;   // pool workspace of this call, freed after its kernels
     if (split) {
+        // Flags are compared with this launch's epoch, so no workspace needs clearing:
+        // whatever an earlier launch (or no launch) left there never matches.
         static std::atomic<unsigned long long> epochs{0x9E3779B97F4A7C15ull};
         const size_t acc_bytes = (size_t)work.G_sk * (nw * 64) * (D / 2) * sizeof(float);
         const size_t ml_bytes = (size_t)work.G_sk * (nw * 64) * 4 * sizeof(float);
         const size_t flag_bytes = (size_t)work.G_sk * sizeof(unsigned long long);
-        e = hipMallocFromPoolAsync(&ws, acc_bytes + ml_bytes + flag_bytes, dev->pool, stream);
-        if (e != hipSuccess) return e;
-        work.ws_acc = static_cast<float*>(ws);
-        work.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + acc_bytes);
-        work.flag = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + acc_bytes + ml_bytes);
+        const size_t need = acc_bytes + ml_bytes + flag_bytes;
+        char* base = nullptr;
+        if (static_ws) {
+            if (dev->scratch == nullptr) return dev->scratch_err != hipSuccess ? dev->scratch_err : hipErrorInvalidSymbol;
+            if (need > kScratchBytes) {
+                if (ws_too_small != nullptr) *ws_too_small = true;
+                return hipErrorInvalidValue;
+            }
+            base = dev->scratch;
+        } else {
+            e = device_info(&dev, true);
+            if (e != hipSuccess) return e;
+            e = hipMallocFromPoolAsync(&ws, need, dev->pool, stream);
+            if (e != hipSuccess) return e;
+            base = static_cast<char*>(ws);
+        }
+        work.ws_acc = reinterpret_cast<float*>(base);
+        work.ws_ml = reinterpret_cast<float*>(base + acc_bytes);
+        work.flag = reinterpret_cast<unsigned long long*>(base + acc_bytes + ml_bytes);
         work.epoch = epochs.fetch_add(1) + 1;
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);

@@ -29,6 +29,9 @@ const char* dtl_status_string(dtl_status s) {
         case DTL_ERR_INVALID_ARG: return "DTL_ERR_INVALID_ARG: invalid argument";
         case DTL_ERR_UNSUPPORTED: return "DTL_ERR_UNSUPPORTED: not supported by this build";
         case DTL_ERR_HIP: return "DTL_ERR_HIP: HIP runtime error at launch";
+        case DTL_ERR_WORKSPACE:
+            return "DTL_ERR_WORKSPACE: the split schedule needs more scratch memory than the "
+                   "library's static workspace holds (attn_fwd_lse_noalloc)";
     }
     return "DTL_ERR_UNKNOWN: unknown status";
 }
@@ -42,7 +45,7 @@ namespace {
 dtl_status attn_call(const void* q, const void* k, const void* v, const float* o_prev,
                      const float* lse_prev, void* o, float* lse, int B, int Nq, int Nkv, int H,
                      int D, int P, float softmax_scale, dtl_dtype o_dtype, bool accum,
-                     hipStream_t stream) {
+                     hipStream_t stream, bool static_ws = false) {
     if (!q || !k || !v || !o || !lse) return DTL_ERR_INVALID_ARG;
     if (accum && (!o_prev || !lse_prev)) return DTL_ERR_INVALID_ARG;
     if (B <= 0 || Nq <= 0 || Nkv <= 0 || H <= 0 || D <= 0) return DTL_ERR_INVALID_ARG;
@@ -76,9 +79,12 @@ dtl_status attn_call(const void* q, const void* k, const void* v, const float* o
     if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)P * B * Nq * H > kIntMax ||
         (long)H * D > (1l << 24))
         return DTL_ERR_INVALID_ARG;
+    bool too_small = false;
     hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, accum ? o_prev : nullptr,
                                         accum ? lse_prev : nullptr, B, Nq, Nkv, H, D, P,
-                                        softmax_scale, o_dtype == DTL_F32, stream);
+                                        softmax_scale, o_dtype == DTL_F32, static_ws,
+                                        &too_small, stream);
+    if (too_small) return DTL_ERR_WORKSPACE;
     return e == hipSuccess ? DTL_OK : DTL_ERR_HIP;
 }
 
@@ -91,6 +97,13 @@ dtl_status attn_fwd_lse(const void* q, const void* k, const void* v, void* o, fl
                         dtl_dtype o_dtype, hipStream_t stream) {
     return attn_call(q, k, v, nullptr, nullptr, o, lse, B, Nq, Nkv, H, D, 1, softmax_scale,
                      o_dtype, false, stream);
+}
+
+dtl_status attn_fwd_lse_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Nq, int Nkv, int H, int D, float softmax_scale,
+                                dtl_dtype o_dtype, hipStream_t stream) {
+    return attn_call(q, k, v, nullptr, nullptr, o, lse, B, Nq, Nkv, H, D, 1, softmax_scale,
+                     o_dtype, false, stream, true);
 }
 
 dtl_status attn_fwd_lse_kv_chunks(const void* q, const void* k, const void* v, void* o_parts,

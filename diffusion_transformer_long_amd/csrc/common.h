@@ -32,10 +32,14 @@ __host__ __device__ __forceinline__ int xcd_contiguous(int pid, int total) {
 // Launchers (validated arguments only; each returns hipGetLastError()).
 // o_prev == nullptr: a fresh result; otherwise continue from (o_prev, lse_prev).  P > 1
 // (fresh results only): the keys are P equal chunks, o and lse hold one result per
-// (chunk, batch), chunk-major.
+// (chunk, batch), chunk-major.  static_ws: a split schedule's workspace is the library's
+// static device array instead of the pool (nothing is allocated); when the schedule
+// needs more than that array holds, nothing is launched, *ws_too_small is set and
+// hipErrorInvalidValue returned.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const float* o_prev, const float* lse_prev, int B, int Nq, int Nkv,
-                           int H, int D, int P, float scale, bool out_f32, hipStream_t stream);
+                           int H, int D, int P, float scale, bool out_f32, bool static_ws,
+                           bool* ws_too_small, hipStream_t stream);
 int merge_max_parts();  // largest P attn_merge_lse accepts
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
                         int P, int B, int N, int H, int D, bool parts_f32, bool out_f32,

@@ -16,8 +16,9 @@
  *     `stream` (allocated before the kernels, freed after them on the same stream; the
  *     pool keeps freed memory for the next call, so repeated calls do not reach the
  *     driver's allocator).  That departs from a library that never allocates: measured,
- *     the split makes Wan2.2-5B-sized attention 3.6% faster.  Per process the library
- *     keeps, per device, its compute-unit count and that pool, created once under a
+ *     the split makes Wan2.2-5B-sized attention 3.6% faster.  Callers that may not
+ *     allocate use attn_fwd_lse_noalloc, whose workspace is a static device array.  Per
+ *     process the library keeps, per device, its compute-unit count and that pool, created once under a
  *     mutex, and a 64-bit launch counter (an atomic) that tells one launch's workspace
  *     flags from another's.
  *     Query tiles have 256 rows (one workgroup per CU) for head_dim 128 with at least
@@ -35,7 +36,8 @@
  *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.
  *   - Calls are asynchronous on `stream` (NULL selects the null stream).  They do
  *     not synchronize, and every pool workspace belongs to one call, so calls on
- *     different streams may run concurrently as long as their buffers do not overlap.
+ *     different streams may run concurrently as long as their buffers do not overlap
+ *     (attn_fwd_lse_noalloc excepted: its calls share one static workspace per device).
  *   - Arguments are validated on the host before anything is launched.  On a
  *     validation error nothing is launched and nothing is written.  DTL_ERR_HIP is
  *     returned when the kernel launch itself reports an error.  Device faults surface,
@@ -55,7 +57,8 @@ typedef enum {
     DTL_OK = 0,
     DTL_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misalignment, overlap, bad divisibility */
     DTL_ERR_UNSUPPORTED = 2,  /* valid request outside what this build implements (head_dim, dtype) */
-    DTL_ERR_HIP = 3           /* the HIP runtime reported an error at launch */
+    DTL_ERR_HIP = 3,          /* the HIP runtime reported an error at launch */
+    DTL_ERR_WORKSPACE = 4     /* attn_fwd_lse_noalloc: the static workspace is too small */
 } dtl_status;
 
 typedef enum {
@@ -97,6 +100,27 @@ dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
                         void *o, float *lse,
                         int B, int Nq, int Nkv, int H, int D,
                         float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_lse_noalloc - attn_fwd_lse for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, result and errors as attn_fwd_lse.  Where attn_fwd_lse takes the split
+ * schedule's workspace from the library's pool, this entry point uses a static device
+ * array of 36 MiB (`scratch` in attn_fwd.hip; each device holds its own copy until the
+ * process ends, its address taken once per device with hipGetSymbolAddress at the
+ * library's first attention call there).  It calls no hipMalloc, hipFree, pool or other
+ * allocating routine.  A schedule that would need more scratch than that (none on a
+ * 256-CU MI355X: at most about 34 MiB) is rejected before anything is launched with
+ * DTL_ERR_WORKSPACE.  Each call leaves its states in the array; the next call needs
+ * none of them cleared (the flags carry a per-launch value).  Every call on one device
+ * shares that device's array: calls that overlap in time on one device (for example on
+ * two streams) race and give undefined results; calls on one stream never overlap.
+ */
+dtl_status attn_fwd_lse_noalloc(const void *q, const void *k, const void *v,
+                                void *o, float *lse,
+                                int B, int Nq, int Nkv, int H, int D,
+                                float softmax_scale, dtl_dtype o_dtype, hipStream_t stream);
 
 /*
  * attn_fwd_lse_accumulate - one round of Ring attention: attention over this call's
