@@ -166,32 +166,42 @@ __device__ __forceinline__ void load_sys4(const float* p, f32x4& a, f32x4& b, f3
 // element is read before it is written, by the same lane), so none of them is restrict.
 // SPLIT = false: one whole tile per workgroup, tiles [tile_base, tile_base + grid).
 // SPLIT = true: the split part, tiles from tile_base on, as stream-K unit ranges.
-template <int D, int NW, bool OUT_F32, bool ACCUM, bool SPLIT>
+// KG = 2 (8 waves, whole tiles only): two groups of 4 waves take the same 128 query rows
+// and each half of the tile's key blocks, with key tiles of their own in LDS; group 1
+// hands its state to group 0 through LDS at the end.  For grids of at most one tile per
+// CU (a Ring round over a short Q block) this puts 8 waves on every busy CU instead of 4.
+template <int D, int NW, int KG, bool OUT_F32, bool ACCUM, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, void* o, float* lse,
                      const float* o_prev, const float* lse_prev,
                      int Nq, int Nkv, int H, int q_batches, int kv_chunks, float scale_log2,
                      int n_qtiles, int tile_base, StreamK work) {
+    static_assert(KG == 1 || (NW == 8 && !SPLIT), "key groups: 8-wave whole tiles");
     constexpr int kThreads = NW * 64;
-    constexpr int kBlockM = NW * 32;   // query rows per workgroup
-    using L = TileLayout<D, NW>;
+    constexpr int kGW = NW / KG;         // waves per key group
+    constexpr int kBlockM = kGW * 32;    // query rows per workgroup
+    using L = TileLayout<D, kGW>;
     // LDS: K and V tiles, two buffers each ([K0 | K1 | V0 | V1], key-major, layout in
     // TileLayout) during the key loop; the output tile on its way to memory after it.
     constexpr int kStageBytes = kBlockM * (4 * D + 16) + kBlockM * 4;   // f32 output staging
-    constexpr int kLdsBytes = 4 * L::kTileBytes > kStageBytes ? 4 * L::kTileBytes : kStageBytes;
+    constexpr int kTilesBytes = KG * 4 * L::kTileBytes;                   // each group: K0 K1 V0 V1
+    constexpr int kLdsBytes = kTilesBytes > kStageBytes ? kTilesBytes : kStageBytes;
     __shared__ __attribute__((aligned(16))) char s_lds[kLdsBytes];
     __shared__ int s_ready;
-    auto sK = [&](int buf) { return s_lds + buf * L::kTileBytes; };
-    auto sV = [&](int buf) { return s_lds + (2 + buf) * L::kTileBytes; };
     auto lds_addr = [&](const char* p) { return (uint32_t)(size_t)(const LDS_AS void*)p; };
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave_all = tid >> 6;
+    const int kg = wave_all / kGW;          // key group (0 with KG = 1)
+    const int wave = wave_all % kGW;        // wave within the group: query rows 32 wave + r
     const int lane = tid & 63;
     const int g = lane >> 5;   // lane half
     const int r = lane & 31;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    char* const s_tiles = s_lds + __builtin_amdgcn_readfirstlane(kg) * 4 * L::kTileBytes;
+    auto sK = [&](int buf) { return s_tiles + buf * L::kTileBytes; };
+    auto sV = [&](int buf) { return s_tiles + (2 + buf) * L::kTileBytes; };
 
     const int tok_stride = H * D;  // elements between consecutive tokens (H*D <= 2^24, checked on the host)
     const long ts_bytes = 2L * tok_stride;
@@ -378,12 +388,20 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     using NOMASK = std::integral_constant<bool, false>;
     using MASKED = std::integral_constant<bool, true>;
 
-    // Key tiles [lo, hi) of the current query tile, continuing the running state.
-    auto run = [&](int lo, int hi) {
-        const bool has_tail = hi == work.n_kv && Nkv % kBlockN != 0;  // the ragged last tile
+    // Key tiles [lo, hi) of the current query tile, continuing the running state.  With
+    // KG = 2, group 0 takes the first ceil(n/2) of them and group 1 the rest; both pass the
+    // same barriers (group 1 one extra when it has one tile fewer).
+    auto run = [&](int lo_all, int hi_all) {
+        int lo = lo_all, hi = hi_all;
+        if constexpr (KG == 2) {
+            const int mid = lo_all + (hi_all - lo_all + 1) / 2;
+            if (kg == 0) hi = mid;
+            else lo = mid;
+        }
+        const bool has_tail = hi > lo && hi == work.n_kv && Nkv % kBlockN != 0;  // the ragged last tile
         const int n_full = (has_tail ? hi - 1 : hi) - lo;
         if (n_full > 0) load_tile(FULL{}, lo * kBlockN, lo & 1);
-        else load_tile(PARTIAL{}, lo * kBlockN, lo & 1);
+        else if (has_tail) load_tile(PARTIAL{}, lo * kBlockN, lo & 1);
         wait_dma();
         // the Q loads are complete too: tell the compiler, which does not see the tile
         // loads, so that it puts no wait for them inside the key loop
@@ -397,6 +415,35 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             ++it;
         }
         if (has_tail) step(PF0{}, MASKED{}, it);
+        if constexpr (KG == 2) {
+            if (hi - lo < (hi_all - lo_all + 1) / 2) __syncthreads();   // group 1's missing step
+            // group 1 hands its state to group 0 (same rows, other keys) through LDS, which
+            // the key tiles no longer need: [wave][acc 16 x D/32 + m, l][lane]
+            float* xs = reinterpret_cast<float*>(s_lds) + wave * ((D / 2) + 2) * 64 + lane;
+            if (kg == 1) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xs[(db * 16 + i) * 64] = acc[db][i];
+                xs[(D / 2) * 64] = m_run;
+                xs[(D / 2 + 1) * 64] = l_run;
+            }
+            __syncthreads();
+            if (kg == 0) {
+                const float m_oth = xs[(D / 2) * 64];
+                const float m_new = fmaxf(m_run, m_oth);   // finite: group 0 saw at least one key
+                const float f_own = __builtin_amdgcn_exp2f(m_run - m_new);
+                const float f_oth = __builtin_amdgcn_exp2f(m_oth - m_new);   // 0 for a group without keys
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[db][i] = acc[db][i] * f_own + xs[(db * 16 + i) * 64] * f_oth;
+                l_run = l_run * f_own + xs[(D / 2 + 1) * 64] * f_oth;
+                m_run = m_new;
+            }
+            __syncthreads();   // LDS is free again
+        }
     };
 
     // Sets the coordinates of query tile `tile`, loads its Q^T fragments (held for the
@@ -442,9 +489,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         char* st = s_lds;
         float* s_wprev = reinterpret_cast<float*>(st + kBlockM * RS);
         const int lrow = wave * 32 + r;                  // this lane's row in the tile
+        // with KG = 2 group 0 holds the whole result (group 1 folded into it)
+        const bool owner = KG == 1 || kg == 0;
         const float l_tot = halves_sum(l_run);
         float w_cur = 1.0f / l_tot, w_prev = 0.0f;
-        if (qrow < Nq) {
+        if (owner && qrow < Nq) {
             const long lidx = ((long)b * H + h) * Nq + qrow;
             const float lse_cur = (m_run + log2f(l_tot)) * 0.693147180559945309f;
             float lse_out = lse_cur;
@@ -465,18 +514,20 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             if (g == 0) lse[lidx] = lse_out;
         }
         // the key loop's last step ended with a barrier: LDS is free
+        if (owner) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
-                                 acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
-                char* dst = st + lrow * RS + (db * 32 + 8 * i4 + 4 * g) * ES;
-                if constexpr (STAGE_F32) *reinterpret_cast<f32x4*>(dst) = x;
-                else *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(x, bf16x4);
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 x = {acc[db][4 * i4] * w_cur, acc[db][4 * i4 + 1] * w_cur,
+                                     acc[db][4 * i4 + 2] * w_cur, acc[db][4 * i4 + 3] * w_cur};
+                    char* dst = st + lrow * RS + (db * 32 + 8 * i4 + 4 * g) * ES;
+                    if constexpr (STAGE_F32) *reinterpret_cast<f32x4*>(dst) = x;
+                    else *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(x, bf16x4);
+                }
+            if constexpr (ACCUM) {
+                if (g == 0) s_wprev[lrow] = w_prev;
             }
-        if constexpr (ACCUM) {
-            if (g == 0) s_wprev[lrow] = w_prev;
         }
         __syncthreads();
         const int row0 = qrow - lrow;                    // the tile's first query row
@@ -648,42 +699,44 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 }
 
-template <int D, int NW, bool OUT_F32, bool ACCUM, bool SPLIT>
+template <int D, int NW, int KG, bool OUT_F32, bool ACCUM, bool SPLIT>
 void launch_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
                 const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
                 int kvc, float scale_log2, int n_qtiles, int grid, int tile_base,
                 const StreamK& work, hipStream_t stream) {
-    attn_fwd_kernel<D, NW, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
+    attn_fwd_kernel<D, NW, KG, OUT_F32, ACCUM, SPLIT><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
         q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, tile_base, work);
 }
 
-template <int D, int NW, bool SPLIT>
+template <int D, int NW, int KG, bool SPLIT>
 void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
               const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
               int kvc, float scale_log2, int n_qtiles, int grid, int tile_base,
               const StreamK& work, bool out_f32, hipStream_t stream) {
     const bool accum = o_prev != nullptr;
     if (out_f32) {
-        if (accum) launch_one<D, NW, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, NW, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, KG, true, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, KG, true, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
     } else {
-        if (accum) launch_one<D, NW, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
-        else launch_one<D, NW, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        if (accum) launch_one<D, NW, KG, false, true, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
+        else launch_one<D, NW, KG, false, false, SPLIT>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, grid, tile_base, work, stream);
     }
 }
 
 // the launches of one schedule: whole tiles first (complete rounds of the slots), then the
 // split part
-template <int D, int NW>
+template <int D, int NW, int KG>
 void launch_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, float* lse,
                      const float* o_prev, const float* lse_prev, int Nq, int Nkv, int H, int qb,
                      int kvc, float scale_log2, int n_qtiles, const StreamK& work, bool out_f32,
                      hipStream_t stream) {
     if (work.n_dp > 0)   // at most one workgroup per slot (persistent over the whole tiles)
-        launch_d<D, NW, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles,
-                               work.n_dp < work.slots ? work.n_dp : work.slots, 0, work, out_f32, stream);
-    if (work.G_sk > 0)
-        launch_d<D, NW, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+        launch_d<D, NW, KG, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles,
+                                   work.n_dp < work.slots ? work.n_dp : work.slots, 0, work, out_f32, stream);
+    if constexpr (KG == 1) {
+        if (work.G_sk > 0)
+            launch_d<D, NW, KG, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+    }
 }
 
 // Static workspace of attn_fwd_lse_noalloc: the states and flags of the split pieces, for
@@ -773,13 +826,24 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
         const long want = strtol(env, nullptr, 10);
         if (D == 128 && (want == 4 || want == 8)) wide = want == 8;
     }
-    const int nw = wide ? 8 : 4;
+    // Two key groups per 8-wave workgroup (128-row tiles, one workgroup per CU) when the
+    // 128-row tiles are at most one per CU, so that every busy CU runs 8 waves rather than
+    // 4 (a Ring round over a short Q block: the FLUX Ring-4 share's 1152-row block is 216
+    // tiles).  DTL_ATTN_KEYSPLIT (tests, tuning) = 0 or 1 turns it off or on wherever it
+    // applies (head_dim 128, 128-row tiles, at least 2 key blocks); never a different result
+    // beyond rounding order.
+    const bool ks_ok = !wide && D == 128 && n_kv >= 2;
+    bool keysplit = ks_ok && (long)((Nq + 127) / 128) * H * B <= dev->cus;
+    if (const char* env = getenv("DTL_ATTN_KEYSPLIT")) keysplit = ks_ok && strtol(env, nullptr, 10) != 0;
+    const int nw = wide || keysplit ? 8 : 4;
+    const int kgr = keysplit ? 2 : 1;
+    const int rows = 32 * nw / kgr;   // query rows per tile
     long slots = (long)(8 / nw) * dev->cus;
     if (const char* env = getenv("DTL_ATTN_SLOTS")) {
         const long want = strtol(env, nullptr, 10);
         if (want > 0 && want < slots) slots = want;
     }
-    const int n_qtiles = (Nq + 32 * nw - 1) / (32 * nw);
+    const int n_qtiles = (Nq + rows - 1) / rows;
     const long tiles = (long)n_qtiles * H * B;   // the caller has checked that this fits an int
     // Split only where whole tiles would leave most of the GPU idle (streamk.h).  A larger
     // remainder already runs well as whole tiles: with fewer workgroups than slots many
@@ -788,6 +852,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // the split part a second launch; with few key blocks per tile (cross-attention's 512
     // keys) those costs exceed the idle tail.
     StreamK work = plan_stream_k(tiles, n_kv, slots);
+    if (keysplit) {   // whole tiles only
+        work.n_dp = (int)tiles;
+        work.G_sk = 0;
+    }
     work.slots = (int)slots;
     // DTL_ATTN_MAX_POLLS (tests) lowers the finalisers' wait for their helpers; at 0 each
     // finaliser computes the rest of its tile itself.  Like the two variables above it
@@ -834,11 +902,13 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     auto kk = static_cast<const uint16_t*>(k);
     auto vv = static_cast<const uint16_t*>(v);
     if (D == 128 && wide)
-        launch_schedule<128, 8>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<128, 8, 1>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
+    else if (D == 128 && keysplit)
+        launch_schedule<128, 8, 2>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     else if (D == 128)
-        launch_schedule<128, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<128, 4, 1>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     else
-        launch_schedule<64, 4>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
+        launch_schedule<64, 4, 1>(qq, kk, vv, o, lse, o_prev, lse_prev, Nq, Nkv, H, Bq, P, scale_log2, n_qtiles, work, out_f32, stream);
     e = hipGetLastError();
     if (ws != nullptr) {
         const hipError_t f = hipFreeAsync(ws, stream);   // stream-ordered: after the kernel

@@ -1,7 +1,8 @@
 """GPU parity of attn_fwd_lse against the fp64 oracle (small and ragged shapes, full oracle).
 
 Shapes span several 128-row query tiles and 64-key tiles with ragged tails in both,
-head_dim 64 and 128, B = 2, one and five heads, bf16 and f32 outputs.  Closed-form
+head_dim 64 and 128, B = 2, one and five heads, bf16 and f32 outputs, each with the
+library's choice of workgroup and with the two-key-group workgroup forced off and on.  Closed-form
 cases: a single key (O equals V bit for bit), identical keys (mean of V), zero
 queries (mean of V, LSE = ln Nkv).  Also: determinism, untouched memory past the
 outputs, and the validation errors raised through the binding.
@@ -46,12 +47,37 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Nq%d_Nkv%d_H%d_D%d_ks%g" % s)
+@pytest.fixture
+def keysplit_env():
+    """Sets DTL_ATTN_KEYSPLIT for one test: "auto" (the library's choice), or two key groups
+    per workgroup forced off ("0") or on ("1") where they apply."""
+    import os
+    old = os.environ.get("DTL_ATTN_KEYSPLIT")
+
+    def set_mode(mode):
+        if mode == "auto":
+            os.environ.pop("DTL_ATTN_KEYSPLIT", None)
+        else:
+            os.environ["DTL_ATTN_KEYSPLIT"] = mode
+    yield set_mode
+    if old is None:
+        os.environ.pop("DTL_ATTN_KEYSPLIT", None)
+    else:
+        os.environ["DTL_ATTN_KEYSPLIT"] = old
+
+
+# key groups apply to head_dim 128 only: the other shapes run with the library's choice
+CASES = [(s, m) for s in SHAPES for m in (("auto", "0", "1") if s[4] == 128 else ("auto",))]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d_Nq%d_Nkv%d_H%d_D%d_ks%g" % c[0] + "_keysplit-" + c[1])
 @pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_attention_matches_oracle(shape, o_dtype):
+def test_attention_matches_oracle(case, o_dtype, keysplit_env):
     import diffusion_transformer_long_amd as dtl
+    shape, mode = case
     B, Nq, Nkv, H, D, ks = shape
-    log("attn_fwd_lse %s o=%s" % (shape, o_dtype))
+    keysplit_env(mode)
+    log("attn_fwd_lse %s o=%s key groups %s" % (shape, o_dtype, mode))
     q, k, v = _inputs(1000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
     o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=o_dtype)
     torch.cuda.synchronize()
