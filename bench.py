@@ -43,19 +43,57 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_flux_N4608_H24_D128_pmc.txt")
-ATTN_SRCS = [os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc", f)
-             for f in ("attn_fwd.hip", "common.h", "streamk.h", "tile_layout.h")] + \
-            [os.path.join(ROOT, "diffusion_transformer_long_amd", "build.py")]   # its compile flags
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "attn_fwd_flux_N4608_H24_D128_pmc.txt")
+_CSRC = os.path.join(ROOT, "diffusion_transformer_long_amd", "csrc")
+_BUILD = os.path.join(ROOT, "diffusion_transformer_long_amd", "build.py")   # the compile flags
+# the sources of each kernel family: a counter summary taken on other sources is stale
+KERNEL_SRCS = {
+    "attn_fwd": [os.path.join(_CSRC, f) for f in ("attn_fwd.hip", "common.h", "streamk.h", "tile_layout.h")] + [_BUILD],
+    "merge": [os.path.join(_CSRC, f) for f in ("merge.hip", "common.h", "fastdiv.h")] + [_BUILD],
+    "permute": [os.path.join(_CSRC, f) for f in ("permute.hip", "runmap.h", "common.h", "fastdiv.h")] + [_BUILD],
+    "norm_rope": [os.path.join(_CSRC, f) for f in ("norm_rope.hip", "common.h", "fastdiv.h")] + [_BUILD],
+}
+ATTN_SRCS = KERNEL_SRCS["attn_fwd"]
+
+
+def source_sha256(family="attn_fwd"):
+    """Hash of one kernel family's sources and build flags."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS[family]:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def attn_source_sha256():
-    """Hash of the attention kernel's sources and build flags; a counter summary taken on
-    other ones is stale."""
-    h = hashlib.sha256()
-    for f in ATTN_SRCS:
-        h.update(open(f, "rb").read())
-    return h.hexdigest()
+    return source_sha256("attn_fwd")
+
+
+def counter_records():
+    """Per-kernel counter figures from the committed rocprofv3 summaries (lines 'json: {...}'
+    in profiles/*_pmc.txt), keyed by (leg, entry); records taken on other kernel sources than
+    the current ones are left out."""
+    import glob
+    out = {}
+    shas = {f: source_sha256(f) for f in KERNEL_SRCS}
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_pmc.txt"))):
+        for line in open(path):
+            if not line.startswith("json: "):
+                continue
+            rec = json.loads(line[6:])
+            if shas.get(rec.get("family")) != rec.get("source_sha256"):
+                continue
+            key = (rec["leg"], rec["entry"])
+            cur = out.setdefault(key, {"summary": "profiles/" + os.path.basename(path)})
+            cur.update({k: v for k, v in rec.items() if k not in ("leg", "entry", "family", "source_sha256")})
+    return out
+
+
+def attach_counters(legs, recs):
+    """Adds each leg's counter figures under legs[leg]["counters"][entry]."""
+    for (leg, entry), rec in recs.items():
+        if leg in legs:
+            legs[leg].setdefault("counters", {})[entry] = rec
 
 
 def err(msg):
@@ -438,6 +476,11 @@ def main():
         err("[bench] cpu baseline (oracle on host cores)")
         cpu = cpu_baseline(w, args.cpu_c5_rows)
         err("[bench] cpu baseline: %s" % cpu)
+
+    recs = counter_records()
+    attach_counters(legs, recs)
+    if roofline is not None and ("headline", "attn") in recs:
+        roofline["counters"] = recs[("headline", "attn")]
 
     line = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at N=4608 and N=27280, 1 GPU",
