@@ -22,12 +22,15 @@
  *     mutex, and a 64-bit launch counter (an atomic) that tells one launch's workspace
  *     flags from another's.
  *     Query tiles have 256 rows (one workgroup per CU) for head_dim 128 with at least
- *     64 key blocks and enough tiles to fill the CUs once, else 128 rows (two
- *     workgroups per CU).
+ *     64 key blocks and enough tiles to fill the CUs once, else 128 rows.  A 128-row
+ *     tile runs in a 4-wave workgroup (two per CU), or, for head_dim 128 when the grid
+ *     holds at most one tile per CU, in an 8-wave workgroup whose two 4-wave key groups
+ *     each take half of the key blocks and fold their partial states in LDS.
  *   - Test and tuning variables, read at every attention call: they change which
  *     workgroup computes which keys, never the result.  DTL_ATTN_SLOTS (a positive
  *     number below the resident workgroup count) schedules as if the GPU held that many
  *     workgroups; DTL_ATTN_WAVES (4 or 8) picks 128- or 256-row tiles for head_dim 128;
+ *     DTL_ATTN_KEYSPLIT (0 or 1) turns the two key groups per 128-row tile off or on;
  *     DTL_ATTN_MAX_POLLS (0 up to the default of 20000) bounds how often a split tile's
  *     finaliser polls for its helpers' published states before it computes their keys
  *     itself (0: at once).
