@@ -851,7 +851,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // workgroup), while every split piece pays a pipeline start, a publish and a merge, and
     // the split part a second launch; with few key blocks per tile (cross-attention's 512
     // keys) those costs exceed the idle tail.
-    StreamK work = plan_stream_k(tiles, n_kv, slots);
+    // DTL_ATTN_SPLIT (tests, tuning) = 0 or 1: never split, or split any remainder; like the
+    // variables above it changes who computes which keys, never the result
+    int force_split = -1;
+    if (const char* env = getenv("DTL_ATTN_SPLIT")) force_split = strtol(env, nullptr, 10) != 0 ? 1 : 0;
+    StreamK work = plan_stream_k(tiles, n_kv, slots, force_split);
     if (keysplit) {   // whole tiles only
         work.n_dp = (int)tiles;
         work.G_sk = 0;

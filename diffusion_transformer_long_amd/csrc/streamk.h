@@ -54,11 +54,13 @@ __host__ __device__ __forceinline__ long sk_first_unit(const StreamK& w, int g) 
 
 // The schedule for `tiles` tiles of n_kv key blocks on `slots` workgroup slots: whole
 // tiles [0, n_dp), the rest split over G_sk workgroups (none when G_sk = 0).
-__host__ __device__ inline StreamK plan_stream_k(long tiles, int n_kv, long slots) {
+// force: -1 the rule above, 0 never split, 1 split any remainder of at least two key blocks
+__host__ __device__ inline StreamK plan_stream_k(long tiles, int n_kv, long slots, int force = -1) {
     StreamK w = {};
     w.n_kv = n_kv;
     const long rem = tiles % slots;
-    const bool split = tiles >= slots && rem > 0 && rem * 4 <= slots && n_kv >= 64;
+    const bool split = tiles >= slots && rem > 0 &&
+                       (force < 0 ? rem * 4 <= slots && n_kv >= 64 : force == 1 && n_kv >= 2);
     w.n_dp = (int)(split ? tiles - rem : tiles);   // a multiple of the slot count when split
     const long W = (tiles - w.n_dp) * n_kv;        // units of the split part
     w.G_sk = (int)(W < slots ? W : slots);

@@ -31,6 +31,8 @@
  *     number below the resident workgroup count) schedules as if the GPU held that many
  *     workgroups; DTL_ATTN_WAVES (4 or 8) picks 128- or 256-row tiles for head_dim 128;
  *     DTL_ATTN_KEYSPLIT (0 or 1) turns the two key groups per 128-row tile off or on;
+ *     DTL_ATTN_SPLIT (0 or 1) never splits the tiles past the last whole round, or splits
+ *     any such remainder (by default only one of at most a quarter of the slots);
  *     DTL_ATTN_MAX_POLLS (0 up to the default of 20000) bounds how often a split tile's
  *     finaliser polls for its helpers' published states before it computes their keys
  *     itself (0: at once).

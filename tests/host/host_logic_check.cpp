@@ -176,6 +176,24 @@ int main() {
         if (wan.n_dp != 5120 || wan.G_sk != 512) { printf("plan wan\n"); ++bad; }
         if (flux.G_sk != 0 || flux.n_dp != 864) { printf("plan flux\n"); ++bad; }
         if (cross.G_sk != 0 || cross.n_dp != 5136) { printf("plan cross\n"); ++bad; }
+        // forced (DTL_ATTN_SPLIT): 1 splits any remainder of tiles with >= 2 key blocks over
+        // at most one workgroup per slot, 0 never splits
+        const dtl::StreamK f1 = dtl::plan_stream_k(432, 72, 256, 1);    // FLUX, 8-wave tiles
+        const dtl::StreamK f0 = dtl::plan_stream_k(2568, 427, 256, 0);  // Wan2.2-5B, 8-wave tiles
+        if (f1.n_dp != 256 || f1.G_sk != 256 || dtl::sk_first_unit(f1, f1.G_sk) != 176L * 72) { printf("plan forced split\n"); ++bad; }
+        if (f0.G_sk != 0 || f0.n_dp != 2568) { printf("plan split off\n"); ++bad; }
+        for (long tiles : tiles_l)
+            for (int n_kv : nkv_l)
+                for (long slots : slots_l) {
+                    const dtl::StreamK w = dtl::plan_stream_k(tiles, n_kv, slots, 1);
+                    const long rem = tiles % slots;
+                    const bool want = tiles >= slots && rem > 0 && n_kv >= 2;
+                    const long W = (tiles - w.n_dp) * (long)n_kv;
+                    const bool ok = want ? (w.n_dp == tiles - rem && w.G_sk == (W < slots ? W : slots) &&
+                                            dtl::sk_first_unit(w, w.G_sk) == W)
+                                         : (w.n_dp == tiles && w.G_sk == 0);
+                    if (!ok) { if (bad < 10) printf("forced plan tiles=%ld n_kv=%d slots=%ld\n", tiles, n_kv, slots); ++bad; }
+                }
     }
     // element source of output element o, written out from each map's definition
     auto direct = [](dtl::PermuteKind kind, long p, long B, long N, long H, long D, long o) -> long {

@@ -6,7 +6,8 @@ compared on whole query tiles plus a seeded row sample.
 
 * tiny ring (N=256, 4 heads of 64, KV 4 x 64): whole oracle; one full-sequence call and
   the ring emulation (4 chunk calls + merge).
-* FLUX (N=4608, 24 x 128, K x 3): whole oracle, all 110592 rows.
+* FLUX (N=4608, 24 x 128, K x 3): whole oracle, all 110592 rows; also with the 176-tile
+  remainder split over every workgroup (stream-K), with and without the finaliser fallback.
 * FLUX Ring-4 share: all four ranks' 1152-row Q blocks against the full K/V as 4 chunks of
   1152, every row, in every form (the default; one attn_fwd_lse call per round + merge;
   all rounds' partials from one attn_fwd_lse_kv_chunks launch + merge; rounds accumulated
@@ -146,6 +147,27 @@ def test_flux_full_sequence_every_row(flux):
     # carries the bar, the bf16 output must be its correct rounding (reading S4)
     _check_full("flux f32-out", o32, lse32, o_ref, l_ref)
     _check_bf16_is_rounded_f32("flux bf16-out", o, o32, o_ref)
+    assert torch.equal(lse, lse32)
+
+
+@pytest.mark.parametrize("polls", [None, "0"], ids=["helpers", "fallback"])
+def test_flux_split_schedule_every_row(flux, monkeypatch, polls):
+    """FLUX with its 176-tile remainder split (DTL_ATTN_SPLIT=1: the stream-K part spread
+    over every workgroup instead of a second round of whole tiles; the library's own rule
+    splits only remainders of at most a quarter of the slots), every row against the oracle.
+    With DTL_ATTN_MAX_POLLS=0 every finaliser computes its helpers' keys itself."""
+    import diffusion_transformer_long_amd as dtl
+    q, k, v, o_ref, l_ref = flux
+    monkeypatch.setenv("DTL_ATTN_SPLIT", "1")
+    if polls is not None:
+        monkeypatch.setenv("DTL_ATTN_MAX_POLLS", polls)
+    log("workload %s, split remainder, polls %s" % (synthetic.FLUX.name, polls or "default"))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = dtl.attn_fwd_lse(qd, kd, vd)
+    o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_full("flux split f32-out", o32, lse32, o_ref, l_ref)
+    _check_bf16_is_rounded_f32("flux split bf16-out", o, o32, o_ref)
     assert torch.equal(lse, lse32)
 
 
