@@ -615,6 +615,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         // accesses, so no cache maintenance is needed: once a workgroup's stores have
         // completed they are in memory, where every XCD reads them.
         const int wg = xcd_contiguous(blockIdx.x, work.G_sk);
+        // this launch's flag value (streamk.h); the launch count changes only after the
+        // launch, so every workgroup reads the same one
+        const unsigned long long flag_val = work.flag == nullptr ? 0ull :
+            sk_flag_value(work.epoch, __hip_atomic_load(work.launch_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
         long u = sk_first_unit(work, wg);
         const long u_end = sk_first_unit(work, wg + 1);
         while (u < u_end) {
@@ -642,7 +646,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                     for (int poll = 0; poll < work.max_polls && !ok; ++poll) {
                         ok = 1;
                         for (int gg = g_first; gg <= g_last; ++gg)
-                            ok &= __hip_atomic_load(work.flag + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == work.epoch;
+                            ok &= __hip_atomic_load(work.flag + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == flag_val;
                         if (!ok) __builtin_amdgcn_s_sleep(8);
                     }
                     s_ready = ok;
@@ -691,7 +695,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are done
                 __syncthreads();
                 if (tid == 0)
-                    __hip_atomic_store(work.flag + wg, work.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    __hip_atomic_store(work.flag + wg, flag_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                 continue;
             }
             finish_tile();
@@ -723,6 +727,14 @@ void launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o, 
     }
 }
 
+// Advances a split workspace's launch count (streamk.h), after the split launch that read it.
+__global__ __launch_bounds__(64) void advance_launch_count_kernel(unsigned long long* ctr) {
+    if (threadIdx.x == 0) {
+        const unsigned long long n = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(ctr, n + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
 // the launches of one schedule: whole tiles first (complete rounds of the slots), then the
 // split part
 template <int D, int NW, int KG>
@@ -734,8 +746,10 @@ void launch_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, vo
         launch_d<D, NW, KG, false>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles,
                                    work.n_dp < work.slots ? work.n_dp : work.slots, 0, work, out_f32, stream);
     if constexpr (KG == 1) {
-        if (work.G_sk > 0)
+        if (work.G_sk > 0) {
             launch_d<D, NW, KG, true>(q, k, v, o, lse, o_prev, lse_prev, Nq, Nkv, H, qb, kvc, scale_log2, n_qtiles, work.G_sk, work.n_dp, work, out_f32, stream);
+            if (work.launch_ctr != nullptr) advance_launch_count_kernel<<<1, 64, 0, stream>>>(work.launch_ctr);
+        }
     }
 }
 
@@ -874,13 +888,15 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     for (int gg = 1; gg < work.G_sk && !split; ++gg) split = sk_first_unit(work, gg) % work.n_kv != 0;
     void* ws = nullptr;   // pool workspace of this call, freed after its kernels
     if (split) {
-        // Flags are compared with this launch's epoch, so no workspace needs clearing:
-        // whatever an earlier launch (or no launch) left there never matches.
+        // Flags are compared with this launch's flag value (streamk.h), so no workspace needs
+        // clearing: whatever an earlier launch, an earlier replay of a captured launch, or
+        // no launch left there never matches.  Layout: [launch count, 16 B | acc | ml | flags].
         static std::atomic<unsigned long long> epochs{0x9E3779B97F4A7C15ull};
+        const size_t ctr_bytes = 16;
         const size_t acc_bytes = (size_t)work.G_sk * (nw * 64) * (D / 2) * sizeof(float);
         const size_t ml_bytes = (size_t)work.G_sk * (nw * 64) * 4 * sizeof(float);
         const size_t flag_bytes = (size_t)work.G_sk * sizeof(unsigned long long);
-        const size_t need = acc_bytes + ml_bytes + flag_bytes;
+        const size_t need = ctr_bytes + acc_bytes + ml_bytes + flag_bytes;
         char* base = nullptr;
         if (static_ws) {
             if (dev->scratch == nullptr) return dev->scratch_err != hipSuccess ? dev->scratch_err : hipErrorInvalidSymbol;
@@ -896,9 +912,10 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
             if (e != hipSuccess) return e;
             base = static_cast<char*>(ws);
         }
-        work.ws_acc = reinterpret_cast<float*>(base);
-        work.ws_ml = reinterpret_cast<float*>(base + acc_bytes);
-        work.flag = reinterpret_cast<unsigned long long*>(base + acc_bytes + ml_bytes);
+        work.launch_ctr = reinterpret_cast<unsigned long long*>(base);
+        work.ws_acc = reinterpret_cast<float*>(base + ctr_bytes);
+        work.ws_ml = reinterpret_cast<float*>(base + ctr_bytes + acc_bytes);
+        work.flag = reinterpret_cast<unsigned long long*>(base + ctr_bytes + acc_bytes + ml_bytes);
         work.epoch = epochs.fetch_add(1) + 1;
     }
     const float scale_log2 = (float)((double)scale * 1.4426950408889634074);

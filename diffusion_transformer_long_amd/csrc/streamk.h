@@ -15,7 +15,7 @@
 //   whole tile                      -> final O and LSE
 //   piece starting inside a tile    -> the raw state (accumulators, reference max, row
 //     (only a range's first piece)     sum per lane) goes to workspace slot g, then flag[g]
-//                                      is set to this launch's epoch
+//                                      is set to this launch's flag value
 //   piece starting a tile, ending   -> the tile's finaliser: after its own keys it waits
 //     inside it (a range's last)       (bounded) for the flags of the workgroups that own
 //                                      the rest of the tile, folds in their states and
@@ -24,9 +24,15 @@
 // but nothing guarantees that they are resident at the same time: the workgroup ids are
 // remapped to XCD-contiguous ranges, so a helper can be dispatched after its finaliser,
 // and another stream or process can hold the compute units it would need.  The wait is
-// therefore bounded (max_polls polls of the flags): if a flag does not carry the epoch
-// in time, the finaliser computes the rest of the tile itself.  The result never depends
-// on timing and every wave terminates.
+// therefore bounded (max_polls polls of the flags): if a flag does not carry the launch's
+// value in time, the finaliser computes the rest of the tile itself.  The result never
+// depends on timing and every wave terminates.
+// The flag value of a launch mixes two counts, so that no flag left in the workspace by
+// another launch matches it and the workspace never needs clearing: `epoch`, a host count
+// of the library's split launches (unique per launch), and the word at `launch_ctr` in the
+// workspace, which every workgroup reads at its start and a one-thread kernel enqueued
+// after the split launch advances.  The second count makes replays of one captured launch
+// (a HIP graph, whose host arguments are frozen) differ from each other as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,10 +48,17 @@ struct StreamK {
     float* ws_acc;              // [G_sk][waves][D/8 stores][64 lanes][4] accumulators
     float* ws_ml;               // [G_sk][threads][4] reference max, row-sum half, 2 unused
     unsigned long long* flag;   // [G_sk]
-    unsigned long long epoch;   // this launch's flag value
+    unsigned long long epoch;   // host count of split launches (see the flag value above)
+    unsigned long long* launch_ctr;   // workspace word advanced after every split launch
     int slots;                  // resident workgroups the schedule assumes (whole-tile grid bound)
     int max_polls;              // a finaliser's bound on polls of its helpers' flags (0: none)
 };
+
+// The flag value of a split launch: its host count mixed with the workspace's launch count.
+__host__ __device__ __forceinline__ unsigned long long sk_flag_value(unsigned long long epoch,
+                                                                     unsigned long long launches) {
+    return epoch ^ (launches * 0x9E3779B97F4A7C15ull);
+}
 
 // First unit of split-part workgroup g (g = G_sk gives W).
 __host__ __device__ __forceinline__ long sk_first_unit(const StreamK& w, int g) {

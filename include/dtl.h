@@ -118,9 +118,12 @@ dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
  * allocating routine.  A schedule that would need more scratch than that (none on a
  * 256-CU MI355X: at most about 34 MiB) is rejected before anything is launched with
  * DTL_ERR_WORKSPACE.  Each call leaves its states in the array; the next call needs
- * none of them cleared (the flags carry a per-launch value).  Every call on one device
- * shares that device's array: calls that overlap in time on one device (for example on
- * two streams) race and give undefined results; calls on one stream never overlap.
+ * none of them cleared: the flags carry a value that differs per launch, including per
+ * replay of a call captured in a HIP graph (a launch count kept in the array and advanced
+ * by a one-thread kernel enqueued after the split launch), so a captured call may be
+ * replayed with new contents in its input buffers.  Every call on one device shares that
+ * device's array: calls that overlap in time on one device (for example on two streams)
+ * race and give undefined results; calls on one stream never overlap.
  */
 dtl_status attn_fwd_lse_noalloc(const void *q, const void *k, const void *v,
                                 void *o, float *lse,
