@@ -380,6 +380,20 @@ def main():
             dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
             dtl.ring_attention(q, k, v, w3.chunks, accumulate=True, o_acc=o_acc, o=o, lse=lse)
         ms_step_acc = timer.time(share_step_acc, reps=10, warmup=2)
+        # the default step captured once in a HIP graph and replayed (launch overhead only
+        # differs; tests/test_gpu_graph.py checks that replays equal the eager step)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            share_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            share_step()
+        torch.cuda.synchronize()
+        ms_step_graph = timer.time(lambda: graph.replay(), reps=10, warmup=2)
+        del graph
         ms_acc = timer.time(lambda: dtl.attn_fwd_lse_accumulate(q, k[:, C:2 * C], v[:, C:2 * C], o_acc, lse),
                             reps=20, warmup=3)
         perm_bytes = 2 * shards.numel() * 2
@@ -390,6 +404,7 @@ def main():
             "step_tflops": round(w3.flops / (ms_step * 1e-3) / 1e12, 2),
             "step_accumulate_ms": round(ms_step_acc, 4),
             "step_accumulate_tflops": round(w3.flops / (ms_step_acc * 1e-3) / 1e12, 2),
+            "step_graph_ms": round(ms_step_graph, 4),
             "step_one_launch_ms": round(ms_step_one, 4),
             "step_one_launch_tflops": round(w3.flops / (ms_step_one * 1e-3) / 1e12, 2),
             "all_chunks_one_launch_ms": round(ms_chunks_one, 4),
