@@ -25,6 +25,7 @@ MUTANTS = {
     "no_normalisation": ("orow[d] /= l;", "orow[d] /= 1.0;"),
     "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
     "exp_sign": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "row_max_not_subtracted": ("            m = s[j];", "            m = 0.0;"),
     "head_offset_dropped": ("const double *kb = k + ((long)b * Nkv * H + h) * D;",
                             "const double *kb = k + ((long)b * Nkv * H) * D;"),
     "batch_stride_uses_nq": ("const double *vb = v + ((long)b * Nkv * H + h) * D;\n            double *orow",

@@ -129,6 +129,32 @@ def test_zero_query_gives_mean_v_and_ln_n(api):
     assert np.max(np.abs(lse - math.log(Nkv))) <= 1e-14
 
 
+def test_one_dominant_key_gives_its_v_exactly(api):
+    """Hard-attention limit: a key whose logit exceeds every other one by more than 745
+    (below which exp underflows to zero in fp64) takes the whole softmax weight, so
+    O is that key's V exactly and LSE its logit; a naive exp of the raw logits (about 1000)
+    would overflow.  The dominant key sits first, inside, and last along the keys."""
+    g = _rng(25)
+    B, Nq, Nkv, H, D = 2, 4, 9, 3, 8
+    q = g.standard_normal((B, Nq, H, D))
+    k = g.standard_normal((B, Nkv, H, D))
+    v = g.standard_normal((B, Nkv, H, D))
+    q[..., 0] = 40.0
+    k[..., 0] = 0.0
+    jstar = np.array([[0, 4, 8], [8, 1, 0]])
+    for b in range(B):
+        for h in range(H):
+            k[b, jstar[b, h], h, 0] = 80.0   # logit gap >= (3200 - 20) / sqrt(8) > 1100
+    o, lse = api.attn(q, k, v)
+    for b in range(B):
+        for h in range(H):
+            j = jstar[b, h]
+            assert np.array_equal(o[b, :, h], np.broadcast_to(v[b, j, h], (Nq, D)))
+            for i in range(Nq):
+                exact = math.fsum(q[b, i, h] * k[b, j, h]) / math.sqrt(D)
+                assert abs(lse[b, h, i] - exact) <= 1e-13 * abs(exact)
+
+
 def test_explicit_scale_argument(api):
     g = _rng(24)
     q = g.standard_normal((1, 4, 1, 8))
