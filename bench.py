@@ -362,10 +362,17 @@ def main():
                               reps=20, warmup=3)
         ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts[rot()], lparts[ctr[0]], o=o, lse=lse), reps, warmup=nrot)
 
-        def share_step():   # one attn_fwd_lse call per round, then the merge
+        def share_step():   # ring_attention's default: here the one-launch partials (a round's
+            # 216 tiles leave workgroup slots idle), then the merge
             dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
             dtl.ring_attention(q, k, v, w3.chunks, o_parts=parts[0], lse_parts=lparts[0], o=o, lse=lse)
         ms_step = timer.time(share_step, reps=10, warmup=2)
+
+        def share_step_rounds():   # one attn_fwd_lse call per round, then the merge
+            dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
+            dtl.ring_attention(q, k, v, w3.chunks, o_parts=parts[0], lse_parts=lparts[0], o=o, lse=lse,
+                               one_launch=False)
+        ms_step_rounds = timer.time(share_step_rounds, reps=10, warmup=2)
 
         def share_step_one():   # the partials of all rounds from one launch, then the merge
             dtl.seq_to_head_permute(perm_in[0], 4, out=perm_out[0])
@@ -407,6 +414,8 @@ def main():
             "step_graph_ms": round(ms_step_graph, 4),
             "step_one_launch_ms": round(ms_step_one, 4),
             "step_one_launch_tflops": round(w3.flops / (ms_step_one * 1e-3) / 1e12, 2),
+            "step_per_round_ms": round(ms_step_rounds, 4),
+            "step_per_round_tflops": round(w3.flops / (ms_step_rounds * 1e-3) / 1e12, 2),
             "all_chunks_one_launch_ms": round(ms_chunks_one, 4),
             "all_chunks_one_launch_tflops": round(w3.flops / (ms_chunks_one * 1e-3) / 1e12, 2),
             "accumulate_chunk_ms": round(ms_acc, 4),
