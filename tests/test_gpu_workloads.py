@@ -14,8 +14,8 @@ compared on whole query tiles plus a seeded row sample.
   in place); the one-launch partials themselves against the oracle over each chunk; the
   Ulysses-4 permute of the four Q shards [4,1,1152,24,128] -> [4,1,4608,6,128], bit-exact.
   These two FLUX workloads reach max|O_ref| = 4.004, where a single bf16 rounding can cost
-  0.0156 > 1e-2 (reading S4): the f32 output is held to the bar and the bf16 output must be
-  exactly the round-to-nearest-even of the f32 output.
+  0.0156 > 1e-2: the f32 output is held to the bar and the bf16 output must be exactly the
+  round-to-nearest-even of the f32 output.
 * Wan2.2-5B (N=27280, 24 x 128): whole first and ragged last query tiles of every head,
   every query tile of the split (stream-K) part of the schedule, and a seeded row sample.
 * Wan2.1-14B Ulysses-8 share (N=75600, 5 x 128, KV 8 x 9450): chunks + merge; whole first
@@ -29,7 +29,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_helpers import assert_close, log, to_np
+from gpu_helpers import assert_close, check_bf16_is_rounded_f32, log, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -54,20 +54,6 @@ def _check_full(name, o, lse, o_ref, l_ref, row0=0):
     offl = lambda f: (lambda idx: f((idx[0], idx[1], idx[2] + row0)))
     assert_close(name + " O", to_np(o), o_ref, labels=off(_bnhd))
     assert_close(name + " LSE", to_np(lse), l_ref, labels=offl(_bhn))
-
-
-def _check_bf16_is_rounded_f32(name, o_bf16, o_f32, o_ref):
-    """Reading S4 for the FLUX-derived workloads (max|O_ref| = 4.004, where one bf16
-    rounding alone can cost 0.0156 > 1e-2): the f32 output carries the bar; the bf16
-    output must be exactly its round-to-nearest-even, element for element.  Its distance
-    from the oracle is reported."""
-    rounded = o_f32.to(torch.bfloat16)
-    same = o_bf16.view(torch.int16) == rounded.view(torch.int16)
-    n_bad = int((~same).sum())
-    d = np.abs(to_np(o_bf16) - o_ref)
-    log("  %-28s bf16 == RNE(f32 output) for %d of %d values; bf16 vs oracle max-abs %.3e mean-abs %.3e"
-        % (name, same.numel() - n_bad, same.numel(), float(d.max()), float(d.mean())))
-    assert n_bad == 0, "%s: %d bf16 values differ from the rounded f32 output" % (name, n_bad)
 
 
 def _check_rows(name, o, lse, q, k, v, rows):
@@ -144,9 +130,9 @@ def test_flux_full_sequence_every_row(flux):
     o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
     torch.cuda.synchronize()
     # max|O| reaches 4 here, where one bf16 rounding alone can cost 0.0156: the f32 output
-    # carries the bar, the bf16 output must be its correct rounding (reading S4)
+    # carries the bar, the bf16 output must be its correct rounding
     _check_full("flux f32-out", o32, lse32, o_ref, l_ref)
-    _check_bf16_is_rounded_f32("flux bf16-out", o, o32, o_ref)
+    check_bf16_is_rounded_f32("flux bf16-out", o, o32, o_ref)
     assert torch.equal(lse, lse32)
 
 
@@ -167,7 +153,7 @@ def test_flux_split_schedule_every_row(flux, monkeypatch, polls):
     o32, lse32 = dtl.attn_fwd_lse(qd, kd, vd, o_dtype=torch.float32)
     torch.cuda.synchronize()
     _check_full("flux split f32-out", o32, lse32, o_ref, l_ref)
-    _check_bf16_is_rounded_f32("flux split bf16-out", o, o32, o_ref)
+    check_bf16_is_rounded_f32("flux split bf16-out", o, o32, o_ref)
     assert torch.equal(lse, lse32)
 
 
@@ -193,7 +179,7 @@ def test_flux_ring4_share_every_rank_every_form(flux):
             o, lse = dtl.ring_attention(qd, kd, vd, w.chunks, **kw)
             torch.cuda.synchronize()
             _check_full("rank%d %s f32-out" % (rank, form), o32, lse32, ref_o, ref_l, row0=r0)
-            _check_bf16_is_rounded_f32("rank%d %s bf16-out" % (rank, form), o, o32, ref_o)
+            check_bf16_is_rounded_f32("rank%d %s bf16-out" % (rank, form), o, o32, ref_o)
             assert torch.equal(lse, lse32)
         o_p, l_p = dtl.attn_fwd_lse_kv_chunks(qd, kd, vd, w.chunks)
         torch.cuda.synchronize()
