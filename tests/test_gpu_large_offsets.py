@@ -125,3 +125,33 @@ def test_merge_past_2_31_elements(out_dtype):
     else:
         assert_bf16_rounding_of("merged O (bf16)", to_np(o_s), o_ref, f32_err)
     assert_close("merged LSE", to_np(l_s), l_ref, max_abs=1e-5, mean_abs=1e-6)
+
+
+def test_permutes_past_4_gib():
+    """seq->head and head->seq permutes of 1 050 000 tokens x 8 heads x 64 eight-byte
+    elements: 4.3 GB each way, byte offsets past 2^32.  The forward permute against the
+    oracle's index map over the whole tensor, bit for bit; the inverse brings it back to
+    the input (the oracle's head->seq undoes its seq->head exactly, as the CPU pins check)."""
+    import diffusion_transformer_long_amd as dtl
+    p, B, N, H, D = 4, 1, 1_050_000, 8, 64
+    nbytes = B * N * H * D * 8
+    assert nbytes > (1 << 32)
+    log("seq_to_head_permute / head_to_seq_permute p=%d B=%d N=%d H=%d D=%d int64 (%.2f GB)"
+        % (p, B, N, H, D, nbytes / 1e9))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(91)
+    x = torch.randint(-(1 << 62), 1 << 62, (p, B, N // p, H, D), generator=g, device=DEV,
+                      dtype=torch.int64)
+    y = dtl.seq_to_head_permute(x, p)
+    torch.cuda.synchronize()
+    x_h = x.cpu().numpy()
+    ref = oracle.permute(x_h, p)
+    same = np.array_equal(y.cpu().numpy(), ref)
+    log("  seq->head equals the oracle's permute: %s" % same)
+    assert same, "seq->head permute differs from the oracle past 4 GiB"
+    del ref
+    z = dtl.head_to_seq_permute(y, p)
+    torch.cuda.synchronize()
+    back = np.array_equal(z.cpu().numpy(), x_h)
+    log("  head->seq gives the input back: %s" % back)
+    assert back, "head->seq permute does not invert seq->head past 4 GiB"
