@@ -139,6 +139,13 @@ class Timer:
         b.synchronize()
         return a.elapsed_time(b) / reps  # ms per call
 
+    def time_batches(self, fn, batches, per_batch, warmup=0):
+        """(median, min) in ms per call over `batches` batches of `per_batch` back-to-back
+        calls, each batch between one pair of events (a pair around every single call
+        would add the events' own ~2 us to kernels of 10-15 us)."""
+        t = sorted(self.time(fn, per_batch, warmup if i == 0 else 0) for i in range(batches))
+        return t[len(t) // 2], t[0]
+
 
 def pmc_traffic():
     """HBM bytes per launch of the headline kernel from the committed rocprofv3 counter
@@ -361,6 +368,10 @@ def main():
         ms_chunk = timer.time(lambda: dtl.attn_fwd_lse(q, k[:, :C], v[:, :C], o=parts[0][0], lse=lparts[0][0]),
                               reps=20, warmup=3)
         ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts[rot()], lparts[ctr[0]], o=o, lse=lse), reps, warmup=nrot)
+        perm_med, perm_min = timer.time_batches(
+            lambda: dtl.seq_to_head_permute(perm_in[rot()], 4, out=perm_out[ctr[0]]), 7, nrot, warmup=nrot)
+        merge_med, merge_min = timer.time_batches(
+            lambda: dtl.attn_merge_lse(parts[rot()], lparts[ctr[0]], o=o, lse=lse), 7, nrot, warmup=nrot)
 
         def share_step():   # ring_attention's default: here the one-launch partials (a round's
             # 216 tiles leave workgroup slots idle), then the merge
@@ -423,7 +434,9 @@ def main():
             "permute_bytes": perm_bytes,
             "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
             "merge_ms": round(ms_merge, 4), "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
-            "merge_bytes": merge_bytes, "rotation_buffers": nrot}
+            "merge_bytes": merge_bytes, "rotation_buffers": nrot,
+            "permute_median_ms": round(perm_med, 4), "permute_min_ms": round(perm_min, 4),
+            "merge_median_ms": round(merge_med, 4), "merge_min_ms": round(merge_min, 4)}
         err("[bench] flux_ring4: %s" % legs["flux_ring4"])
         del qf, k, v, shards, q, perm_out, perm_in, parts, lparts, o, lse
 
@@ -441,6 +454,7 @@ def main():
         ms_chunk = timer.time(lambda: dtl.attn_fwd_lse(q, k[:, :C], v[:, :C], o=parts[0], lse=lparts[0]),
                               reps=4, warmup=1)
         ms_merge = timer.time(lambda: dtl.attn_merge_lse(parts, lparts, o=o, lse=lse), reps=10, warmup=2)
+        merge_med, merge_min = timer.time_batches(lambda: dtl.attn_merge_lse(parts, lparts, o=o, lse=lse), 5, 2)
         ms_step = timer.time(lambda: dtl.ring_attention(q, k, v, w5.chunks, o_parts=parts, lse_parts=lparts,
                                                          o=o, lse=lse), reps=2, warmup=1)
         o_acc = parts[0]
@@ -458,7 +472,8 @@ def main():
             "accumulate_chunk_ms": round(ms_acc, 4),
             "chunk_attn_ms": round(ms_chunk, 4), "chunk_attn_tflops": round(chunk_flops / (ms_chunk * 1e-3) / 1e12, 2),
             "merge_ms": round(ms_merge, 4), "merge_gbs": round(merge_bytes / (ms_merge * 1e-3) / 1e9, 1),
-            "merge_bytes": merge_bytes, "merge_frac_of_hbm": round(merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "merge_bytes": merge_bytes, "merge_frac_of_hbm": round(merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "merge_median_ms": round(merge_med, 4), "merge_min_ms": round(merge_min, 4)}
         err("[bench] wan14b_u8: %s" % legs["wan14b_u8"])
         del q, k, v, parts, lparts, o, lse
 
@@ -470,9 +485,11 @@ def main():
 
         def one(name, fn, x, out, shape):
             ms = timer.time(lambda: fn(x, p, out=out), reps=10, warmup=2)
+            med, mn = timer.time_batches(lambda: fn(x, p, out=out), 5, 2)
             nbytes = 2 * x.numel() * x.element_size()
             res[name] = {"shape": shape, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                         "bytes": nbytes, "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         "bytes": nbytes, "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "median_ms": round(med, 4), "min_ms": round(mn, 4)}
             err("[bench]   %s: %s" % (name, res[name]))
 
         x = torch.empty((p, 1, Ns, H, D), dtype=torch.bfloat16, device=dev).normal_()
