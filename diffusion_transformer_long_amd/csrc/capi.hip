@@ -79,6 +79,9 @@ dtl_status attn_call(const void* q, const void* k, const void* v, const float* o
     if (tiles > kIntMax || (long)B * Nkv * H > kIntMax || (long)P * B * Nq * H > kIntMax ||
         (long)H * D > (1l << 24))
         return DTL_ERR_INVALID_ARG;
+    // the kernel forms query rows (up to Nq + 254 in a last 256-row tile) and key indices (up
+    // to Nkv + 63 for the next key tile) as ints
+    if ((long)Nq > kIntMax - 256 || (long)Nkv > kIntMax - 256) return DTL_ERR_INVALID_ARG;
     bool too_small = false;
     hipError_t e = dtl::launch_attn_fwd(q, k, v, o, lse, accum ? o_prev : nullptr,
                                         accum ? lse_prev : nullptr, B, Nq, Nkv, H, D, P,

@@ -96,10 +96,11 @@ typedef enum {
  * Arithmetic: bf16 products with f32 accumulation for q.k and p.v; the softmax
  * weights are computed in f32 and rounded to bf16, and both the p.v product and the
  * row sum (the denominator, accumulated in f32) use those same rounded weights.
- * Errors: DTL_ERR_INVALID_ARG for null pointers, any size <= 0, a scale that is not
- * finite and positive, misaligned pointers, or an output overlapping an input or the
- * other output; DTL_ERR_UNSUPPORTED for D not in {64, 128} or another o_dtype;
- * DTL_ERR_HIP when a launch or the workspace allocation fails.
+ * Errors: DTL_ERR_INVALID_ARG for null pointers, any size <= 0, Nq or Nkv above
+ * 2^31 - 257, B*Nq*H or B*Nkv*H rows or query tiles (of 128 rows) above 2^31 - 1, H*D
+ * above 2^24, a scale that is not finite and positive, misaligned pointers, or an output
+ * overlapping an input or the other output; DTL_ERR_UNSUPPORTED for D not in {64, 128} or
+ * another o_dtype; DTL_ERR_HIP when a launch or the workspace allocation fails.
  */
 dtl_status attn_fwd_lse(const void *q, const void *k, const void *v,
                         void *o, float *lse,

@@ -67,6 +67,14 @@ def test_attn_fwd_lse_validation():
     assert _attn(lib, D=96) == UNS
     assert _attn(lib, D=256) == UNS
     assert _attn(lib, dt=7) == UNS
+    # size limits, with the buffers 2^44 bytes apart so that no overlap decides: Nq or Nkv
+    # past 2^31 - 257 (query rows and key indices are ints in the kernel), B*Nkv*H rows past
+    # 2^31 - 1, H*D past 2^24
+    far = dict(q=1 << 44, k=2 << 44, v=3 << 44, o=4 << 44, lse=5 << 44)
+    imax = 2 ** 31 - 1
+    for kw in ({"Nq": imax - 255, "H": 1}, {"Nkv": imax - 255, "H": 1},
+               {"Nkv": 2 ** 30, "H": 2}, {"H": 2 ** 17 + 1, "Nq": 1, "Nkv": 1}):
+        assert _attn(lib, **far, **kw) == INV, kw
 
 
 def test_attn_fwd_lse_kv_chunks_validation():
