@@ -12,6 +12,8 @@ on the same inputs, bit for bit; the eager results are compared with the oracle.
   captured call's inputs switched between two sets before each replay.
 * The FLUX Ring-4 share step (Ulysses-4 permute, the four rounds' partials from one
   launch, the merge), a launch-bound sequence of three kernels.
+* The same share's four rounds as four launches: accumulated in place into an f32 running
+  result, or per-round partials and the merge.
 """
 import os
 
@@ -152,3 +154,46 @@ def test_flux_ring4_share_step_replays_in_a_graph():
     assert perm.cpu().view(torch.int16).numpy().tobytes() == ref.tobytes()
     _, l_ref = oracle.attn(qf[:, :w.Nq].contiguous(), k, v)
     assert_close("graph step LSE", to_np(lse), l_ref)
+
+
+@pytest.mark.parametrize("form", ["accumulate", "per_round"])
+def test_flux_ring4_rounds_replay_in_a_graph(form):
+    """The FLUX Ring-4 share's four rounds as four launches captured in one graph: folded
+    into an f32 running result in place (accumulate), or as per-round partials and the merge.
+    Each replay starts from buffers the eager work in between has overwritten."""
+    import diffusion_transformer_long_amd as dtl
+    w = synthetic.FLUX_RING4
+    log("graph replay: %s, rounds %s" % (w.name, form))
+    qf, k, v = synthetic.workload_qkv(synthetic.FLUX)
+    qd = qf[:, :w.Nq].contiguous().to(DEV)
+    kd, vd = k.to(DEV), v.to(DEV)
+    acc = torch.empty((1, w.Nq, w.H, w.D), dtype=torch.float32, device=DEV)
+    parts = torch.empty((w.chunks, 1, w.Nq, w.H, w.D), dtype=torch.float32, device=DEV)
+    lparts = torch.empty((w.chunks, 1, w.H, w.Nq), dtype=torch.float32, device=DEV)
+    o = torch.empty((1, w.Nq, w.H, w.D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((1, w.H, w.Nq), dtype=torch.float32, device=DEV)
+
+    def step():
+        if form == "accumulate":
+            dtl.ring_attention(qd, kd, vd, w.chunks, accumulate=True, o_acc=acc, o=o, lse=lse)
+        else:
+            dtl.ring_attention(qd, kd, vd, w.chunks, o_parts=parts, lse_parts=lparts, o=o, lse=lse,
+                               one_launch=False)
+
+    step()
+    torch.cuda.synchronize()
+    o_e, l_e = o.clone(), lse.clone()
+    g = _capture(step)
+    for r in range(REPLAYS):
+        for t in (acc, parts, lparts):
+            t.fill_(float("nan"))
+        o.zero_()
+        lse.fill_(float("-inf"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = torch.equal(o, o_e) and torch.equal(lse, l_e)
+        log("  replay %d: %s the eager step" % (r, "equals" if ok else "DIFFERS FROM"))
+        assert ok, "replay %d differs from the eager step" % r
+    _, l_ref = oracle.attn(qf[:, :w.Nq].contiguous(), k, v)
+    assert_close("graph rounds LSE", to_np(lse), l_ref)
