@@ -26,7 +26,7 @@
  *     tile runs in a 4-wave workgroup (two per CU), or, for head_dim 128 when the grid
  *     holds at most one tile per CU, in an 8-wave workgroup whose two 4-wave key groups
  *     each take half of the key blocks and fold their partial states in LDS.
- *   - Test and tuning variables, read at every attention call: they change which
+ *   - Test and tuning variables, read at every call they apply to: they change which
  *     workgroup computes which keys, never the result.  DTL_ATTN_SLOTS (a positive
  *     number below the resident workgroup count) schedules as if the GPU held that many
  *     workgroups; DTL_ATTN_WAVES (4 or 8) picks 128- or 256-row tiles for head_dim 128;
@@ -35,7 +35,9 @@
  *     any such remainder (by default only one of at most a quarter of the slots);
  *     DTL_ATTN_MAX_POLLS (0 up to the default of 20000) bounds how often a split tile's
  *     finaliser polls for its helpers' published states before it computes their keys
- *     itself (0: at once).
+ *     itself (0: at once).  DTL_MERGE_KERNEL=lds makes attn_merge_lse take its LDS kernel
+ *     for every shape instead of the row kernel it uses for P in {2, 4, 8} and D in
+ *     {64, 128} (read at every merge call; the same result bit for bit).
  *   - Tensors are dense and row-major in the shapes given; there are no strides.
  *     Every pointer must be 16-byte aligned.
  *   - bf16 is IEEE bfloat16 stored as 16-bit words; f32 is IEEE binary32.

@@ -88,9 +88,11 @@ def test_merge_identity_empty_parts_order():
     assert l_n is None and torch.equal(o_n, o_d)
 
 
-def test_merge_bf16_parts():
+@pytest.mark.parametrize("P", [3, 4])
+def test_merge_bf16_parts(P):
+    """bf16 partials: P = 3 takes the LDS kernel, P = 4 the row kernel."""
     import diffusion_transformer_long_amd as dtl
-    o_p, l_p = _parts(6, 3, 1, 40, 2, 128)
+    o_p, l_p = _parts(6 + P, P, 1, 40, 2, 128)
     ob = torch.from_numpy(o_p).to(torch.bfloat16)
     o, lse = dtl.attn_merge_lse(ob.to(DEV), torch.from_numpy(l_p).to(DEV), out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -325,3 +327,41 @@ def test_ulysses4_flux_end_to_end():
     b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
     assert_close("ulysses4 O (%d rows)" % len(rows), o.float().cpu().numpy()[b, i, h].astype(np.float64), o_ref)
     assert_close("ulysses4 LSE (%d rows)" % len(rows), lse.cpu().numpy()[b, h, i].astype(np.float64), l_ref)
+
+
+@pytest.mark.parametrize("P,D", [(2, 64), (4, 128), (8, 128), (4, 64)])
+@pytest.mark.parametrize("parts_dtype", [torch.float32, torch.bfloat16], ids=["f32parts", "bf16parts"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_merge_row_kernel_equals_lds_kernel(P, D, parts_dtype, out_dtype):
+    """The row kernel (P in {2, 4, 8}, D in {64, 128}) against the LDS kernel
+    (DTL_MERGE_KERNEL=lds) on the same inputs, bit for bit: a third of the rows have an
+    empty part holding NaN, some rows have every part empty, and the row count is not a
+    multiple of either kernel's rows per workgroup."""
+    import os
+    import diffusion_transformer_long_amd as dtl
+    B, N, H = 2, 301, 3
+    log("merge row kernel vs LDS kernel P=%d D=%d parts %s out %s" % (P, D, parts_dtype, out_dtype))
+    o_p, l_p = _parts(900 + P + D, P, B, N, H, D)
+    l_p[1, :, :, ::3] = -np.inf
+    o_p[1, :, ::3] = np.nan
+    l_p[:, 1, 0, 7:11] = -np.inf
+    od = torch.from_numpy(o_p).to(parts_dtype).to(DEV)
+    ld = torch.from_numpy(l_p).to(DEV)
+    o_r, l_r = dtl.attn_merge_lse(od, ld, out_dtype=out_dtype)
+    old = os.environ.get("DTL_MERGE_KERNEL")
+    os.environ["DTL_MERGE_KERNEL"] = "lds"
+    try:
+        o_l, l_l = dtl.attn_merge_lse(od, ld, out_dtype=out_dtype)
+    finally:
+        if old is None:
+            os.environ.pop("DTL_MERGE_KERNEL", None)
+        else:
+            os.environ["DTL_MERGE_KERNEL"] = old
+    torch.cuda.synchronize()
+    iv = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(o_r.view(iv), o_l.view(iv)), "O differs between the two merge kernels"
+    assert torch.equal(l_r.view(torch.int32), l_l.view(torch.int32)), "LSE differs between the two merge kernels"
+    o_ref, l_ref = oracle.merge(od.float().cpu().numpy(), l_p)
+    finite = np.isfinite(l_ref)
+    assert np.all(to_np(o_r)[~np.broadcast_to(finite.transpose(0, 2, 1)[..., None], o_ref.shape)] == 0)
+    assert_close("row kernel LSE (finite rows)", to_np(l_r)[finite], l_ref[finite], max_abs=1e-5, mean_abs=1e-6)
