@@ -831,9 +831,12 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // DTL_ATTN_SLOTS (tests, tuning) schedules as if the GPU held that many workgroups; it
     // changes which tiles are split, never the result.  It may only lower the count.
     const int n_kv = (Nkv + kBlockN - 1) / kBlockN;
-    // 8-wave workgroups (256-row tiles, one per CU) for long key ranges whose tiles fill
-    // at least one round; 4-wave ones (128 rows, two per CU) otherwise
-    bool wide = D == 128 && n_kv >= 64 && (long)((Nq + 255) / 256) * H * B >= dev->cus;
+    // 8-wave workgroups (256-row tiles, one per CU) for key ranges of more than 16 blocks
+    // whose tiles fill at least one round; 4-wave ones (128 rows, two per CU) otherwise.
+    // Measured on full grids (27280 queries, 24 heads): 8 waves take 1.027x the 4-wave time
+    // at 8 key blocks, 1.011x at 12, 1.000x at 16, 0.966x at 24 and 32, 0.978x at 48;
+    // 0.924x at 4608 x 1152 and 0.962x for the FLUX Ring-4 share's four chunks in one launch.
+    bool wide = D == 128 && n_kv > 16 && (long)((Nq + 255) / 256) * H * B >= dev->cus;
     // DTL_ATTN_WAVES (tests, tuning) = 4 or 8 picks the workgroup size for head_dim 128;
     // like DTL_ATTN_SLOTS it changes the schedule, never the result
     if (const char* env = getenv("DTL_ATTN_WAVES")) {
