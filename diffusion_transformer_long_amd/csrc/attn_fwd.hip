@@ -832,11 +832,14 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* o,
     // changes which tiles are split, never the result.  It may only lower the count.
     const int n_kv = (Nkv + kBlockN - 1) / kBlockN;
     // 8-wave workgroups (256-row tiles, one per CU) for key ranges of more than 16 blocks
-    // whose tiles fill at least one round; 4-wave ones (128 rows, two per CU) otherwise.
-    // Measured on full grids (27280 queries, 24 heads): 8 waves take 1.027x the 4-wave time
-    // at 8 key blocks, 1.011x at 12, 1.000x at 16, 0.966x at 24 and 32, 0.978x at 48;
-    // 0.924x at 4608 x 1152 and 0.962x for the FLUX Ring-4 share's four chunks in one launch.
-    bool wide = D == 128 && n_kv > 16 && (long)((Nq + 255) / 256) * H * B >= dev->cus;
+    // whose 128-row tiles would be more than one per CU; 4-wave ones (128 rows, two per CU)
+    // otherwise.  Measured on full grids (27280 queries, 24 heads), 8 waves take 1.027x the
+    // 4-wave time at 8 key blocks, 1.011x at 12, 1.000x at 16, 0.966x at 24 and 32, 0.978x
+    // at 48; 0.924x at 4608 x 1152 and 0.962x for the FLUX Ring-4 share's four chunks in one
+    // launch.  Between one and two 128-row tiles per CU some CU runs two of them, which takes
+    // longer than one 256-row tile even with CUs left idle: 0.89-0.93x at 2304 x 4608,
+    // 3072 x 4608 (16 heads), 1536 x 27280, 2560 x 2048 and 4608 x 4608 (12 heads).
+    bool wide = D == 128 && n_kv > 16 && (long)((Nq + 127) / 128) * H * B > dev->cus;
     // DTL_ATTN_WAVES (tests, tuning) = 4 or 8 picks the workgroup size for head_dim 128;
     // like DTL_ATTN_SLOTS it changes the schedule, never the result
     if (const char* env = getenv("DTL_ATTN_WAVES")) {

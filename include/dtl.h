@@ -22,8 +22,8 @@
  *     mutex, and a 64-bit launch counter (an atomic) that tells one launch's workspace
  *     flags from another's.
  *     Query tiles have 256 rows (one workgroup per CU) for head_dim 128 with more than
- *     16 key blocks of 64 (Nkv > 1024) and enough tiles to fill the CUs once, else 128
- *     rows.  A 128-row tile runs in a 4-wave workgroup (two per CU), or, for head_dim 128
+ *     16 key blocks of 64 (Nkv > 1024) when 128-row tiles would be more than one per CU,
+ *     else 128 rows.  A 128-row tile runs in a 4-wave workgroup (two per CU), or, for head_dim 128
  *     when the grid
  *     holds at most one tile per CU, in an 8-wave workgroup whose two 4-wave key groups
  *     each take half of the key blocks and fold their partial states in LDS.

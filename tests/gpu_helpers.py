@@ -93,3 +93,22 @@ def check_bf16_is_rounded_f32(name, o_bf16, o_f32, o_ref):
     log("  %-28s bf16 == RNE(f32 output) for %d of %d values; bf16 vs oracle max-abs %.3e mean-abs %.3e"
         % (name, same.numel() - n_bad, same.numel(), float(d.max()), float(d.mean())))
     assert n_bad == 0, "%s: %d bf16 values differ from the rounded f32 output" % (name, n_bad)
+
+
+def kernels_run(fn):
+    """Names of the GPU kernels fn() launches, as torch's profiler records them, shortened
+    to the name and template arguments (for example 'attn_fwd_kernel<128, 4, 1, false,
+    false, true>')."""
+    import re
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    out = set()
+    for e in prof.events():
+        m = re.search(r"(\w+_kernel(?:<[^()]*>)?)\(", e.name)
+        if m:
+            out.add(m.group(1))
+    return out

@@ -33,7 +33,7 @@ REPLAYS = 3
 
 @pytest.fixture
 def env():
-    names = ("DTL_ATTN_SLOTS", "DTL_ATTN_WAVES")
+    names = ("DTL_ATTN_SLOTS", "DTL_ATTN_WAVES", "DTL_ATTN_KEYSPLIT")
     saved = {n: os.environ.get(n) for n in names}
     yield os.environ
     for n, val in saved.items():
@@ -77,6 +77,7 @@ def test_noalloc_split_call_replays_in_a_graph(env, nw, o_dtype):
     # the last tile's 65 key blocks split over every slot
     env["DTL_ATTN_SLOTS"] = "8" if nw == 4 else "4"
     env["DTL_ATTN_WAVES"] = str(nw)
+    env["DTL_ATTN_KEYSPLIT"] = "0"   # 9 tiles of 128 rows would otherwise take two key groups
     B, Nq, Nkv, H, D = 1, 1152, 4100, 1, 128
     log("graph replay: noalloc split, %d waves, o %s" % (nw, o_dtype))
     sets = [_inputs(11, B, Nq, Nkv, H, D, k_scale=2.0), _inputs(12, B, Nq, Nkv, H, D, k_scale=2.0)]

@@ -122,9 +122,10 @@ def test_dominant_key_whole_tiles(env, sched, o_dtype):
 
 SPLITS = [
     # name, environment: one head's last 128-row tile (1152 x 4100) split over the slots
-    ("split_4_waves", {"DTL_ATTN_SLOTS": "8", "DTL_ATTN_WAVES": "4"}),
+    ("split_4_waves", {"DTL_ATTN_SLOTS": "8", "DTL_ATTN_WAVES": "4", "DTL_ATTN_KEYSPLIT": "0"}),
     ("split_8_waves", {"DTL_ATTN_SLOTS": "4", "DTL_ATTN_WAVES": "8"}),
-    ("split_no_polls", {"DTL_ATTN_SLOTS": "8", "DTL_ATTN_WAVES": "4", "DTL_ATTN_MAX_POLLS": "0"}),
+    ("split_no_polls", {"DTL_ATTN_SLOTS": "8", "DTL_ATTN_WAVES": "4", "DTL_ATTN_KEYSPLIT": "0",
+                        "DTL_ATTN_MAX_POLLS": "0"}),
 ]
 
 

@@ -11,7 +11,10 @@ The cases cover a tile split
 over 8 workgroups, ranges crossing tile boundaries, the ragged last key block inside a
 split tile, B = 2, D = 64 and 128, 4- and 8-wave workgroups (DTL_ATTN_WAVES), bf16 and
 f32 outputs, and the accumulate entry point with rows that hold no keys yet.  Every result
-is compared with the oracle.
+is compared with the oracle.  These grids hold at most one 128-row tile per CU, where the
+library would run two key groups per workgroup (whole tiles only), so the 4-wave cases also
+set DTL_ATTN_KEYSPLIT=0; the main cases check from torch's profiler that the split launch
+ran exactly where the schedule splits.
 """
 import os
 
@@ -21,7 +24,7 @@ import torch
 
 import oracle
 import synthetic
-from gpu_helpers import assert_close, log, to_np
+from gpu_helpers import assert_close, kernels_run, log, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -30,15 +33,21 @@ DEV = torch.device("cuda:0")
 
 @pytest.fixture
 def slots():
-    old = os.environ.get("DTL_ATTN_SLOTS")
+    """DTL_ATTN_SLOTS, with DTL_ATTN_KEYSPLIT=0: these grids hold at most one 128-row tile
+    per CU, where the library would otherwise run two key groups per workgroup (whole tiles
+    only) instead of the 4-wave split schedule under test."""
+    names = ("DTL_ATTN_SLOTS", "DTL_ATTN_KEYSPLIT")
+    saved = {n: os.environ.get(n) for n in names}
 
     def set_slots(n):
         os.environ["DTL_ATTN_SLOTS"] = str(n)
+        os.environ["DTL_ATTN_KEYSPLIT"] = "0"
     yield set_slots
-    if old is None:
-        os.environ.pop("DTL_ATTN_SLOTS", None)
-    else:
-        os.environ["DTL_ATTN_SLOTS"] = old
+    for n, val in saved.items():
+        if val is None:
+            os.environ.pop(n, None)
+        else:
+            os.environ[n] = val
 
 
 @pytest.fixture
@@ -89,6 +98,26 @@ CASES = [
 ]
 
 
+def _expect_split(n, B, Nq, Nkv, H, rows):
+    """Whether the schedule splits: at least one full round of tiles over the n slots, a
+    remainder of at most a quarter of them, at least 64 key blocks per tile."""
+    tiles = -(-Nq // rows) * H * B
+    rem = tiles % n
+    return tiles >= n and rem > 0 and rem * 4 <= n and -(-Nkv // 64) >= 64
+
+
+def _run_checked(fn, D, nw, split):
+    """fn() under the profiler: the attention kernels it ran must be the D, nw-wave ones,
+    with the split part (SPLIT = true) exactly when the schedule splits."""
+    out = {}
+    names = kernels_run(lambda: out.setdefault("r", fn()))
+    attn = sorted(x for x in names if x.startswith("attn_fwd_kernel<"))
+    log("  kernels: %s" % ", ".join(attn))
+    assert attn and all(x.startswith("attn_fwd_kernel<%d, %d, 1," % (D, nw)) for x in attn), attn
+    assert any(x.endswith("true>") for x in attn) == split, "split expected: %s, ran %s" % (split, attn)
+    return out["r"]
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "slots%d_B%d_Nq%d_Nkv%d_H%d_D%d" % c[:6])
 @pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_split_schedule_matches_oracle(slots, case, o_dtype):
@@ -97,7 +126,9 @@ def test_split_schedule_matches_oracle(slots, case, o_dtype):
     log("split schedule slots=%d %s o=%s" % (n, case[1:], o_dtype))
     q, k, v = _inputs(3000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
     slots(n)
-    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=o_dtype)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = _run_checked(lambda: dtl.attn_fwd_lse(qd, kd, vd, o_dtype=o_dtype), D, 4,
+                          _expect_split(n, B, Nq, Nkv, H, 128))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attn(q, k, v)
     assert_close("O", to_np(o), o_ref)
@@ -123,7 +154,9 @@ def test_split_schedule_8_waves_matches_oracle(slots, waves, case, o_dtype):
     q, k, v = _inputs(5000 + Nq + Nkv, B, Nq, Nkv, H, D, ks)
     slots(n)
     waves(8)
-    o, lse = dtl.attn_fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), o_dtype=o_dtype)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = _run_checked(lambda: dtl.attn_fwd_lse(qd, kd, vd, o_dtype=o_dtype), D, 8,
+                          _expect_split(n, B, Nq, Nkv, H, 256))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attn(q, k, v)
     assert_close("O", to_np(o), o_ref)
