@@ -318,8 +318,10 @@ def main():
         ms = timer.time(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), reps=max(3, args.steps // 4),
                         warmup=2)
         tf = w5.flops / (ms * 1e-3) / 1e12
+        med, mn = timer.time_batches(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), 5, 1)
         legs["wan5b"] = {"workload": w5.name, "attn_ms": round(ms, 4), "attn_tflops": round(tf, 2),
-                         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                         "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "attn_median_ms": round(med, 4), "attn_min_ms": round(mn, 4)}
         err("[bench] wan5b: %.3f ms, %.1f TFLOP/s" % (ms, tf))
         del q, k, v, o, lse
 
@@ -331,11 +333,13 @@ def main():
         o = torch.empty((wc.B, wc.Nq, wc.H, wc.D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((wc.B, wc.H, wc.Nq), dtype=torch.float32, device=dev)
         ms = timer.time(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), reps=20, warmup=3)
+        med, mn = timer.time_batches(lambda: dtl.attn_fwd_lse(q, k, v, o=o, lse=lse), 7, 5)
         tf = wc.flops / (ms * 1e-3) / 1e12
         nbytes = 2 * wc.B * (2 * wc.Nq + 2 * wc.Nkv) * wc.H * wc.D + 4 * wc.B * wc.H * wc.Nq
         legs["wan5b_cross"] = {"workload": wc.name, "attn_ms": round(ms, 4), "attn_tflops": round(tf, 2),
                                "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                               "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+                               "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                               "attn_median_ms": round(med, 4), "attn_min_ms": round(mn, 4)}
         err("[bench] wan5b_cross: %s" % legs["wan5b_cross"])
         del q, k, v, o, lse
 
